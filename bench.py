@@ -1,0 +1,315 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X tree-verify attention (split-KV flash-decode over an MLA paged KV cache).
+
+Prints ONE JSON line. A step is one verify call: the partial kernel plus the combine kernel over
+one batch of seeded synthetic inputs already resident in HBM. The default workload is the ragged
+B=4 batch with prefixes 4096/32768/120000/185000, q_len 16, H 64, nsplit 64, scattered slots in a
+2M-row pool. `value` is the effective KV bandwidth (sum of L_b * 1152 bytes per step / time per
+step); `ms_per_step` is the wall-clock time per step over the timed region.
+
+The roofline object covers the dominant kernel (the partial kernel): its algorithmic flops (or
+bytes, when the workload sits below the MFMA ridge) per launch over its average duration, timed
+with HIP events on the stream it runs on. cpu_baseline times the fp64 CPU oracle on a bounded
+sample of rows of the same workload and scales it to the whole step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verify-attn µs/step + effective KV GB/s (% HBM/MFMA roofline) at 16k/65k/185k"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+RIDGE = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)  # flop per byte
+
+
+def algorithmic(inp):
+    """Algorithmic bytes and flops of one step: every KV row once, 4 index bytes and q_len mask bytes
+    per column, the queries once, out and lse once; flops = q_len * H * L * (576 + 512) * 2."""
+    lengths = [p + inp.q_len for p in inp.prefixes]
+    total_L = sum(lengths)
+    rows = inp.B * inp.q_len * inp.H
+    kv = total_L * 1152
+    partial_bytes = kv + total_L * 4 + inp.q_len * total_L + rows * 576 * 2
+    step_bytes = partial_bytes + rows * 512 * 2 + rows * 4
+    flops = inp.q_len * inp.H * total_L * (576 + 512) * 2
+    return dict(total_L=total_L, kv_bytes=kv, partial_bytes=partial_bytes, step_bytes=step_bytes, flops=flops)
+
+
+class Workload:
+    """Device buffers of one configuration and the library calls on them."""
+
+    def __init__(self, wl, layout, nsplit, dev):
+        import numpy as np
+        import torch
+
+        import speculative_decoding_mla_split_amd as pkg
+        import workloads as W
+
+        self.pkg, self.torch, self.np, self.W = pkg, torch, np, W
+        self.wl, self.layout, self.nsplit = wl, layout, nsplit
+        self.inp = W.make_inputs(wl, layout=layout)
+        inp = self.inp
+        self.dev = dev
+
+        def t(a, bf16=False):
+            a = np.ascontiguousarray(a)
+            if bf16:
+                return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+            return torch.from_numpy(a).to(dev)
+
+        pool = torch.full((inp.N, 576), W.BF16_NAN, dtype=torch.int16, device=dev)
+        pool[torch.from_numpy(inp.ref_slots.astype(np.int64)).to(dev)] = torch.from_numpy(
+            inp.ref_rows.view(np.int16)).to(dev)
+        self.pool = pool.view(torch.bfloat16)
+        self.q_nope, self.q_rope = t(inp.q_nope, True), t(inp.q_rope, True)
+        self.kv_indptr, self.kv_indices = t(inp.kv_indptr), t(inp.kv_indices)
+        self.out_cache_loc, self.custom_mask, self.mask_indptr = t(inp.out_cache_loc), t(inp.custom_mask), t(
+            inp.mask_indptr)
+        self.ws_bytes = pkg.workspace_size(inp.B, inp.q_len, inp.H, nsplit)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.out = torch.empty((inp.B, inp.q_len, inp.H, 512), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((inp.B, inp.q_len, inp.H), dtype=torch.float32, device=dev)
+        self.alg = algorithmic(inp)
+
+    def partial(self, stream):
+        inp = self.inp
+        rc = self.pkg.partial_raw(self.q_nope.data_ptr(), self.q_rope.data_ptr(), self.pool.data_ptr(), inp.N,
+                                  self.kv_indptr.data_ptr(), self.kv_indices.data_ptr(), self.out_cache_loc.data_ptr(),
+                                  self.custom_mask.data_ptr(), self.mask_indptr.data_ptr(), inp.B, inp.q_len, inp.H,
+                                  inp.scale, self.nsplit, self.ws.data_ptr(), self.ws_bytes, stream.cuda_stream)
+        assert rc == 0, self.pkg.status_string(rc)
+
+    def combine(self, stream):
+        inp = self.inp
+        rc = self.pkg.combine_raw(self.ws.data_ptr(), self.ws_bytes, inp.B, inp.q_len, inp.H, self.nsplit,
+                                  self.out.data_ptr(), self.lse.data_ptr(), stream.cuda_stream)
+        assert rc == 0, self.pkg.status_string(rc)
+
+    def step(self, stream):
+        self.partial(stream)
+        self.combine(stream)
+
+    def time_steps(self, stream, steps, warmup, scrub=None):
+        """Eager steps with HIP events around each kernel; returns per-step wall and kernel times (us)."""
+        torch = self.torch
+        for _ in range(warmup):
+            self.step(stream)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        if scrub is None:
+            t0 = time.perf_counter()
+            for k in range(steps):
+                evs[k][0].record(stream)
+                self.partial(stream)
+                evs[k][1].record(stream)
+                self.combine(stream)
+                evs[k][2].record(stream)
+            torch.cuda.synchronize()
+            wall = (time.perf_counter() - t0) / steps * 1e6
+        else:
+            for k in range(steps):
+                scrub.fill_(k & 0xFF)  # evict the KV rows from L2 and the MALL (outside the events)
+                evs[k][0].record(stream)
+                self.partial(stream)
+                evs[k][1].record(stream)
+                self.combine(stream)
+                evs[k][2].record(stream)
+            torch.cuda.synchronize()
+            wall = None
+        part = [evs[k][0].elapsed_time(evs[k][1]) * 1e3 for k in range(steps)]
+        comb = [evs[k][1].elapsed_time(evs[k][2]) * 1e3 for k in range(steps)]
+        stepu = [evs[k][0].elapsed_time(evs[k][2]) * 1e3 for k in range(steps)]
+        return wall, part, comb, stepu
+
+    def graph_us_per_step(self, stream, replays):
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                self.step(stream)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(replays):
+            g.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / replays * 1e6
+
+    def parity(self, nrows, seed=0):
+        """Sampled rows (corners + random) of the last step against the fp64 oracle."""
+        import oracle
+        np, W, torch = self.np, self.W, self.torch
+        torch.cuda.synchronize()
+        inp = self.inp
+        rng = np.random.default_rng(seed)
+        rows = {(b, i, h) for b in range(inp.B) for i in (0, inp.q_len - 1) for h in (0, inp.H - 1)}
+        while len(rows) < nrows:
+            rows.add((int(rng.integers(inp.B)), int(rng.integers(inp.q_len)), int(rng.integers(inp.H))))
+        rows = np.array(sorted(rows), np.int32)
+        pool, ki, oc = W.compact_inputs(inp)
+        ref_out, ref_lse = oracle.attn_rows(*oracle.inputs_args(inp, pool, ki, oc), rows=rows)
+        got = self.out.float().cpu().numpy().astype(np.float64)[rows[:, 0], rows[:, 1], rows[:, 2]]
+        got_lse = self.lse.cpu().numpy().astype(np.float64)[rows[:, 0], rows[:, 1], rows[:, 2]]
+        err = float(np.abs(got - ref_out).max())
+        rel = float(np.linalg.norm(got - ref_out) / np.linalg.norm(ref_out))
+        lerr = float(np.abs(got_lse - ref_lse).max())
+        ok = err <= 1e-2 and rel <= 5e-3 and lerr <= 1e-3
+        return dict(rows=int(len(rows)), max_abs=err, rel_l2=rel, lse_abs=lerr, ok=bool(ok))
+
+
+def cpu_baseline(inp, alg, wl_name, seconds):
+    """The fp64 oracle on the host cores, on rows sampled from the workload, scaled to a full step."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+    pool, ki, oc = W.compact_inputs(inp)
+    args = oracle.inputs_args(inp, pool, ki, oc)
+    cores = len(os.sched_getaffinity(0))
+    lengths = [p + inp.q_len for p in inp.prefixes]
+    rng = np.random.default_rng(1)
+    done_rows, done_cols, spent = 0, 0, 0.0
+    batch = max(cores, 1)
+    while spent < seconds:
+        rows = np.stack([rng.integers(0, inp.B, batch), rng.integers(0, inp.q_len, batch),
+                         rng.integers(0, inp.H, batch)], axis=1).astype(np.int32)
+        t0 = time.perf_counter()
+        oracle.attn_rows(*args, rows=rows, nthreads=cores)
+        spent += time.perf_counter() - t0
+        done_rows += len(rows)
+        done_cols += int(sum(lengths[b] for b in rows[:, 0]))
+    all_cols = inp.q_len * inp.H * sum(lengths)
+    t_step = spent * all_cols / done_cols
+    value = alg["kv_bytes"] / t_step / 1e9
+    return dict(value=value, unit="GB/s", cores=cores, kind="oracle",
+                sample=f"{done_rows} random (b,i,h) rows of {wl_name} ({done_cols} row-columns, {spent:.1f} s); "
+                       f"full step estimated at {t_step:.1f} s by column count", us_per_step=t_step * 1e6)
+
+
+def stats(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return dict(median=xs[n // 2], p10=xs[max(0, int(n * 0.1))], p90=xs[min(n - 1, int(n * 0.9))],
+                mean=sum(xs) / n)
+
+
+def roofline_for(wk, part_us):
+    alg = wk.alg
+    ai = alg["flops"] / alg["partial_bytes"]
+    t = part_us * 1e-6
+    if ai > RIDGE:
+        ach = alg["flops"] / t / 1e12
+        return dict(bound="mfma", achieved=ach, peak=MFMA_BF16_PEAK_TFS, unit="TFLOP/s", frac=ach / MFMA_BF16_PEAK_TFS,
+                    traffic=None, algorithmic_flops=alg["flops"], algorithmic_bytes=alg["partial_bytes"],
+                    arithmetic_intensity=ai)
+    ach = alg["partial_bytes"] / t / 1e9
+    return dict(bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s", frac=ach / HBM_PEAK_GBS, traffic=None,
+                algorithmic_flops=alg["flops"], algorithmic_bytes=alg["partial_bytes"], arithmetic_intensity=ai)
+
+
+def step_floor_us(alg):
+    return max(alg["step_bytes"] / (HBM_PEAK_GBS * 1e9), alg["flops"] / (MFMA_BF16_PEAK_TFS * 1e12)) * 1e6
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="ragged4_185k_h64")
+    ap.add_argument("--layout", default=None)
+    ap.add_argument("--nsplit", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true", help="skip the 16k/65k configuration sweep")
+    ap.add_argument("--parity-rows", type=int, default=48)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the verify attention is a single-GPU "
+                                   "kernel here (multi-GPU sharding is a design note, not built)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    wl = W.CONFIGS[args.config]
+    layout = args.layout or wl.layout
+    nsplit = args.nsplit or wl.nsplits[-1]
+    stream = torch.cuda.Stream(device=dev)
+    print(f"[bench] {wl.name} layout={layout} nsplit={nsplit}", file=sys.stderr, flush=True)
+    wk = Workload(wl, layout, nsplit, dev)
+    wall, part, comb, stepu = wk.time_steps(stream, args.steps, args.warmup)
+    print(f"[bench] timed {args.steps} steps: {wall:.1f} us/step", file=sys.stderr, flush=True)
+    parity = wk.parity(args.parity_rows)
+    graph_us = wk.graph_us_per_step(stream, max(args.steps, 20))
+    part_s, comb_s = stats(part), stats(comb)
+    alg = wk.alg
+    value = alg["kv_bytes"] / (wall * 1e-6) / 1e9
+    floor = step_floor_us(alg)
+    result = {
+        "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall / 1e3, "us_per_step": wall, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "prefixes": list(wl.prefixes), "q_len": wl.q_len, "H": wl.H,
+                   "pool_rows": wl.N, "layout": layout, "nsplit": nsplit, "seed": wl.seed,
+                   "scale": "1/sqrt(192)", "parallelism": "single GPU"},
+        "roofline": roofline_for(wk, part_s["mean"]),
+        "kernels_us": {"partial": part_s, "combine": comb_s, "step_events": stats(stepu)},
+        "graph_us_per_step": graph_us,
+        "step_floor_us": floor, "step_roofline_frac": floor / wall,
+        "tflops_step": alg["flops"] / (wall * 1e-6) / 1e12,
+        "parity_sampled": parity,
+    }
+    main_inp = wk.inp
+    del wk
+    torch.cuda.empty_cache()
+
+    if not args.no_others:
+        others = []
+        scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        for name, lay, ns in (("16k_h64", "contiguous", 16), ("16k_h64", "scattered", 16),
+                              ("16k_h64", "scattered", 32), ("16k_h64", "scattered", 64),
+                              ("65k_h8", "scattered", 16), ("65k_h8", "scattered", 64), ("4k_h64", "scattered", 16)):
+            print(f"[bench] sweep {name} {lay} nsplit={ns}", file=sys.stderr, flush=True)
+            ow = Workload(W.CONFIGS[name], lay, ns, dev)
+            hot_wall, hp, hc, hs = ow.time_steps(stream, 30, 5)
+            _, cp, cc, cs = ow.time_steps(stream, 20, 2, scrub=scrub)
+            a = ow.alg
+            fl = step_floor_us(a)
+            others.append({
+                "workload": name, "layout": lay, "nsplit": ns,
+                "hot_us_per_step": hot_wall, "hot_kv_GBs": a["kv_bytes"] / (hot_wall * 1e-6) / 1e9,
+                "cold_step_us_median": stats(cs)["median"],
+                "cold_kv_GBs": a["kv_bytes"] / (stats(cs)["median"] * 1e-6) / 1e9,
+                "partial_us_hot": stats(hp)["mean"], "partial_us_cold": stats(cp)["median"],
+                "combine_us_hot": stats(hc)["mean"],
+                "step_floor_us": fl, "roofline_frac_hot": fl / hot_wall, "roofline_frac_cold": fl / stats(cs)["median"],
+                "partial_roofline": roofline_for(ow, stats(hp)["mean"]),
+            })
+            del ow
+            torch.cuda.empty_cache()
+        result["other_configs"] = others
+        del scrub
+
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(main_inp, alg, wl.name, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,148 @@
+/*
+ * mla_verify.h -- C ABI of the MI355X (gfx950) tree-verify attention over an MLA paged KV cache.
+ *
+ * One call computes, for every request b, draft token i and head h, softmax attention of the
+ * query [q_nope | q_rope] (576 values) over the request's columns: its prefix tokens followed by
+ * its q_len draft tokens, each a 576-wide bf16 row of the KV pool (512 latent values, which are
+ * also the value vector, then 64 rope values), restricted to the columns the tree mask makes
+ * visible. It runs as a split-KV flash-decode: nsplit partials per request, each holding online
+ * softmax statistics of one contiguous column slice, then a log-sum-exp combine.
+ *
+ * Sources (the pages this interface is built from):
+ *  - "From Capture Safety to MoE Ceiling" (magik.net llmopt seg_66/chunk_3), section
+ *    "The Architecture of Capture Safety": a fixed NSPLIT with chunk bounds computed on the
+ *    device from the actual KV length and cheap early exit of empty splits; prefix slots read
+ *    from kv_indices and draft slots from out_cache_loc, chosen by position relative to the
+ *    prefix length (no host-side concatenation); the raw custom_mask with mask_indptr offsets
+ *    indexed inline; a workspace allocated outside the step; no host synchronisation,
+ *    allocation or copy inside the step, so the step can be captured into a graph.
+ *  - "The Custom sm_120 Verify Kernel" (magik.net llmopt seg_66/chunk_2), section "Building
+ *    the Custom Kernel": per-split partial softmax statistics in global scratch and a second
+ *    reduction kernel; section "The Debugging Gauntlet": draft columns come after the prefix
+ *    columns and a mask row is prefix + q_len bytes wide; only the first B mask offsets matter.
+ *
+ * Conventions for every entry point:
+ *  - Device pointers refer to memory of the current HIP device; host scalars are passed by value.
+ *  - The caller owns every buffer. The library never allocates, frees, copies through the host
+ *    or synchronises; it only enqueues kernels on `stream` (NULL = the default stream).
+ *  - Argument errors are detected on the host and returned as a negative status before any HIP
+ *    call is made. A failed kernel launch returns MLA_VERIFY_ERR_LAUNCH.
+ *  - The call is asynchronous and can be captured into a hipGraph: the launch configuration
+ *    depends only on (B, q_len, H, nsplit), and every length is read on the device.
+ *  - There is no global mutable state: calls on different streams with different workspaces
+ *    may run concurrently.
+ */
+#ifndef MLA_VERIFY_H
+#define MLA_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MLA_VERIFY_OK = 0,
+    MLA_VERIFY_ERR_NULL = -1,      /* a required pointer is NULL */
+    MLA_VERIFY_ERR_SHAPE = -2,     /* B, q_len, H or N out of range, or scale not finite */
+    MLA_VERIFY_ERR_NSPLIT = -3,    /* nsplit outside [1, MLA_VERIFY_MAX_NSPLIT] */
+    MLA_VERIFY_ERR_WORKSPACE = -4, /* workspace NULL, misaligned or smaller than required */
+    MLA_VERIFY_ERR_LAUNCH = -5     /* the HIP runtime refused a kernel launch */
+} mla_verify_status;
+
+#define MLA_VERIFY_LATENT 512          /* latent (value) width of a KV row */
+#define MLA_VERIFY_ROPE 64             /* rope width of a KV row */
+#define MLA_VERIFY_ROW 576             /* bf16 values per KV pool row (1152 bytes) */
+#define MLA_VERIFY_MAX_NSPLIT 1024
+#define MLA_VERIFY_WORKSPACE_ALIGN 256 /* required alignment of the workspace pointer */
+
+/*
+ * Bytes of workspace mla_verify_attn needs for these sizes ("From Capture Safety to MoE
+ * Ceiling", "The Architecture of Capture Safety": the workspace is allocated once, outside
+ * the step). It holds one partial per (request, split, draft token, head): the running max
+ * and sum (2 floats) and the unnormalised 512-wide accumulator (512 floats).
+ * Returns 0 when an argument is out of range (B, q_len, H < 1; nsplit outside [1, 1024]).
+ */
+size_t mla_verify_attn_workspace_size(int B, int q_len, int H, int nsplit);
+
+/* Static, NUL-terminated description of a status code. Never NULL. */
+const char *mla_verify_status_string(int status);
+
+/*
+ * Tree-verify attention for B requests (sources above).
+ *
+ *  q_nope        bf16 [B, q_len, H, 512], dense row-major: latent part of each query.
+ *  q_rope        bf16 [B, q_len, H, 64], dense row-major: rope part of each query.
+ *  kv_pool       bf16 [N, 576], dense row-major: one row per token slot (page size 1);
+ *                columns [0, 512) are the latent (key and value), [512, 576) the rope (key).
+ *  N             number of pool rows. A slot outside [0, N) is clamped into range, so no read
+ *                leaves the pool; the result of a row that reads such a slot is unspecified.
+ *  kv_indptr     int32 [B + 1]: the prefix of request b is kv_indices[kv_indptr[b] ..
+ *                kv_indptr[b+1]); prefix length P_b = kv_indptr[b+1] - kv_indptr[b] >= 0.
+ *                kv_indptr[0] need not be 0. A negative P_b is treated as 0.
+ *  kv_indices    int32: prefix slots. May be NULL only if every P_b is 0.
+ *  out_cache_loc int32 [B * q_len]: slot of draft token t of request b at b*q_len + t.
+ *  custom_mask   uint8: for request b, q_len rows of L_b = P_b + q_len bytes starting at
+ *                mask_indptr[b]; byte custom_mask[mask_indptr[b] + i*L_b + c] != 0 makes
+ *                column c (prefix columns first, then draft columns) visible to draft token i.
+ *  mask_indptr   int32, at least B entries (a CSR array of B + 1 is accepted; entry B is
+ *                never read): start offset of each request's mask.
+ *  B, q_len, H   requests, draft tokens per request, query heads; all >= 1.
+ *  scale         multiplies the 576-wide dot product before the softmax (finite).
+ *  nsplit        number of contiguous column splits per request, in [1, 1024]. Split s covers
+ *                columns [s*chunk, min(L_b, (s+1)*chunk)) with chunk = ceil(L_b / nsplit)
+ *                rounded up to a multiple of 32; splits past L_b exit at once.
+ *  workspace     device scratch of at least mla_verify_attn_workspace_size(B, q_len, H, nsplit)
+ *                bytes, aligned to 256 bytes. No initialisation is needed; its contents after
+ *                the call are unspecified. Calls that share a workspace must be ordered (same
+ *                stream, or synchronised).
+ *  out           bf16 [B, q_len, H, 512]: softmax-weighted sum of the visible latent rows,
+ *                rounded to nearest even. A row with no visible column gets zeros.
+ *  lse           fp32 [B, q_len, H]: natural-log log-sum-exp of the visible scaled scores
+ *                (-inf for a row with no visible column).
+ *  stream        HIP stream the two kernels are enqueued on.
+ *
+ * Returns MLA_VERIFY_OK or a negative mla_verify_status. Behaviour is undefined when a device
+ * array is shorter than described above (for example a mask shorter than its offsets imply).
+ */
+int mla_verify_attn(const void *q_nope, const void *q_rope, const void *kv_pool, int64_t N,
+                    const int32_t *kv_indptr, const int32_t *kv_indices,
+                    const int32_t *out_cache_loc, const uint8_t *custom_mask,
+                    const int32_t *mask_indptr, int B, int q_len, int H, float scale, int nsplit,
+                    void *workspace, size_t workspace_bytes, void *out, float *lse,
+                    hipStream_t stream);
+
+/*
+ * The two phases of mla_verify_attn as separate calls (same arguments and rules as above).
+ * mla_verify_attn == mla_verify_attn_partial followed by mla_verify_attn_combine on one stream.
+ *
+ * mla_verify_attn_partial runs the split kernel ("The Custom sm_120 Verify Kernel", section
+ * "Building the Custom Kernel": each block takes one contiguous column slice and writes partial
+ * online-softmax statistics to global scratch) and leaves the nsplit partials in `workspace`.
+ * mla_verify_attn_combine runs the reduction kernel of the same section on those partials and
+ * writes out and lse. Between the two calls the workspace holds, for every (b, s, i, h), the
+ * split's running max m (base-2 units of the scaled score, -inf for an empty or fully masked
+ * split), its sum l of 2^(score*log2(e) - m) and its unnormalised 512-wide accumulator, laid out
+ * as float2 ml[B][nsplit][q_len*H] followed (at the next 256-byte boundary) by
+ * float acc[B][nsplit][q_len*H][512]. A caller may move these partials between the two calls
+ * (for example to combine partials computed for different column ranges elsewhere); the combine
+ * needs only this layout. Calls with the same (B, q_len, H, nsplit) must be used for both.
+ */
+int mla_verify_attn_partial(const void *q_nope, const void *q_rope, const void *kv_pool, int64_t N,
+                            const int32_t *kv_indptr, const int32_t *kv_indices,
+                            const int32_t *out_cache_loc, const uint8_t *custom_mask,
+                            const int32_t *mask_indptr, int B, int q_len, int H, float scale,
+                            int nsplit, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+int mla_verify_attn_combine(const void *workspace, size_t workspace_bytes, int B, int q_len, int H,
+                            int nsplit, void *out, float *lse, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_VERIFY_H */

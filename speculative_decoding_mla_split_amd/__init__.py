@@ -1,0 +1,125 @@
+"""MI355X tree-verify attention over an MLA paged KV cache (split-KV flash-decode).
+
+A thin ctypes binding of libmla_verify.so (C ABI declared in include/mla_verify.h). It only
+checks and marshals arguments: every step of the computation runs in the library's HIP kernels.
+There is no fallback path; calling without the built library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmla_verify.so")
+LATENT, ROPE, ROW = 512, 64, 576
+MAX_NSPLIT = 1024
+WORKSPACE_ALIGN = 256
+
+STATUS = {0: "MLA_VERIFY_OK", -1: "MLA_VERIFY_ERR_NULL", -2: "MLA_VERIFY_ERR_SHAPE",
+          -3: "MLA_VERIFY_ERR_NSPLIT", -4: "MLA_VERIFY_ERR_WORKSPACE", -5: "MLA_VERIFY_ERR_LAUNCH"}
+
+_lib = None
+
+
+class MlaVerifyError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def library() -> ctypes.CDLL:
+    """Load libmla_verify.so (built by __graft_entry__.build() or build.py)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m speculative_decoding_mla_split_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        lib.mla_verify_attn_workspace_size.argtypes = [i32, i32, i32, i32]
+        lib.mla_verify_attn_workspace_size.restype = sz
+        lib.mla_verify_status_string.argtypes = [i32]
+        lib.mla_verify_status_string.restype = ctypes.c_char_p
+        lib.mla_verify_attn.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, vp, i32, i32, i32, f32, i32, vp, sz, vp,
+                                        vp, vp]
+        lib.mla_verify_attn.restype = i32
+        lib.mla_verify_attn_partial.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, vp, i32, i32, i32, f32, i32, vp,
+                                                sz, vp]
+        lib.mla_verify_attn_partial.restype = i32
+        lib.mla_verify_attn_combine.argtypes = [vp, sz, i32, i32, i32, i32, vp, vp, vp]
+        lib.mla_verify_attn_combine.restype = i32
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return library().mla_verify_status_string(int(status)).decode()
+
+
+def workspace_size(B: int, q_len: int, H: int, nsplit: int) -> int:
+    """Bytes of workspace verify_attn needs (0 if an argument is out of range)."""
+    return int(library().mla_verify_attn_workspace_size(int(B), int(q_len), int(H), int(nsplit)))
+
+
+def attn_raw(q_nope, q_rope, kv_pool, N, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
+             B, q_len, H, scale, nsplit, workspace, workspace_bytes, out, lse, stream) -> int:
+    """Direct call of mla_verify_attn with integer device addresses; returns the status."""
+    return int(library().mla_verify_attn(q_nope, q_rope, kv_pool, int(N), kv_indptr, kv_indices, out_cache_loc,
+                                         custom_mask, mask_indptr, int(B), int(q_len), int(H), float(scale),
+                                         int(nsplit), workspace, int(workspace_bytes), out, lse, stream))
+
+
+def partial_raw(q_nope, q_rope, kv_pool, N, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
+                B, q_len, H, scale, nsplit, workspace, workspace_bytes, stream) -> int:
+    """Direct call of mla_verify_attn_partial with integer device addresses; returns the status."""
+    return int(library().mla_verify_attn_partial(q_nope, q_rope, kv_pool, int(N), kv_indptr, kv_indices,
+                                                 out_cache_loc, custom_mask, mask_indptr, int(B), int(q_len), int(H),
+                                                 float(scale), int(nsplit), workspace, int(workspace_bytes), stream))
+
+
+def combine_raw(workspace, workspace_bytes, B, q_len, H, nsplit, out, lse, stream) -> int:
+    """Direct call of mla_verify_attn_combine with integer device addresses; returns the status."""
+    return int(library().mla_verify_attn_combine(workspace, int(workspace_bytes), int(B), int(q_len), int(H),
+                                                 int(nsplit), out, lse, stream))
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def verify_attn(q_nope, q_rope, kv_pool, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
+                scale: float, nsplit: int, workspace, out, lse, stream=None) -> None:
+    """Tree-verify attention on torch device tensors (no copies, no host synchronisation).
+
+    q_nope bf16 [B,q_len,H,512], q_rope bf16 [B,q_len,H,64], kv_pool bf16 [N,576],
+    kv_indptr int32 [B+1], kv_indices int32, out_cache_loc int32 [B*q_len], custom_mask uint8/bool,
+    mask_indptr int32 [>=B], workspace uint8 [>= workspace_size(...)], out bf16 [B,q_len,H,512],
+    lse float32 [B,q_len,H]. stream: a torch.cuda.Stream (default: the current stream).
+    """
+    import torch
+
+    B, q_len, H, d = q_nope.shape
+    _need(d == LATENT and tuple(q_rope.shape) == (B, q_len, H, ROPE), "q_nope/q_rope shapes")
+    _need(kv_pool.dim() == 2 and kv_pool.shape[1] == ROW, "kv_pool must be [N, 576]")
+    _need(tuple(out.shape) == (B, q_len, H, LATENT) and tuple(lse.shape) == (B, q_len, H), "out/lse shapes")
+    for name, t, dt in (("q_nope", q_nope, torch.bfloat16), ("q_rope", q_rope, torch.bfloat16),
+                        ("kv_pool", kv_pool, torch.bfloat16), ("out", out, torch.bfloat16),
+                        ("lse", lse, torch.float32), ("kv_indptr", kv_indptr, torch.int32),
+                        ("kv_indices", kv_indices, torch.int32), ("out_cache_loc", out_cache_loc, torch.int32),
+                        ("mask_indptr", mask_indptr, torch.int32), ("workspace", workspace, torch.uint8)):
+        _need(t.dtype == dt, f"{name} must be {dt}")
+        _need(t.is_cuda, f"{name} must be a device tensor")
+        _need(t.is_contiguous(), f"{name} must be contiguous")
+    _need(custom_mask.dtype in (torch.uint8, torch.bool) and custom_mask.is_cuda and custom_mask.is_contiguous(),
+          "custom_mask must be a contiguous uint8/bool device tensor")
+    _need(kv_indptr.numel() >= B + 1 and mask_indptr.numel() >= B and out_cache_loc.numel() >= B * q_len,
+          "index array lengths")
+    if stream is None:
+        stream = torch.cuda.current_stream(q_nope.device)
+    rc = attn_raw(q_nope.data_ptr(), q_rope.data_ptr(), kv_pool.data_ptr(), kv_pool.shape[0],
+                  kv_indptr.data_ptr(), kv_indices.data_ptr() if kv_indices.numel() else None,
+                  out_cache_loc.data_ptr(), custom_mask.data_ptr(), mask_indptr.data_ptr(), B, q_len, H, scale,
+                  nsplit, workspace.data_ptr(), workspace.numel(), out.data_ptr(), lse.data_ptr(),
+                  stream.cuda_stream)
+    if rc != 0:
+        raise MlaVerifyError(rc, status_string(rc))

@@ -1,0 +1,90 @@
+"""C-ABI checks that need no GPU: symbols, workspace sizing, argument validation before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import speculative_decoding_mla_split_amd as pkg
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mla_verify.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_verify_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = pkg.library()
+    names = _declared_functions()
+    assert set(names) == {"mla_verify_attn", "mla_verify_attn_partial", "mla_verify_attn_combine",
+                          "mla_verify_attn_workspace_size", "mla_verify_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_workspace_size():
+    # (m, l) float2 + 512 fp32 per (b, split, token, head), each region padded to 256 bytes
+    rows = 2 * 16 * 9 * 8
+    expect = -(-rows * 8 // 256) * 256 + -(-rows * 2048 // 256) * 256
+    assert pkg.workspace_size(2, 9, 8, 16) == expect
+    assert pkg.workspace_size(0, 9, 8, 16) == 0
+    assert pkg.workspace_size(1, 0, 8, 16) == 0
+    assert pkg.workspace_size(1, 9, 0, 16) == 0
+    assert pkg.workspace_size(1, 9, 8, 0) == 0
+    assert pkg.workspace_size(1, 9, 8, 1025) == 0
+    assert pkg.workspace_size(1, 9, 8, 1024) > 0
+
+
+def test_status_strings():
+    for code in range(-5, 1):
+        assert pkg.status_string(code)
+    assert pkg.status_string(7) == "unknown status"
+
+
+FAKE = 0x10000  # a non-null address that is never dereferenced: every call below fails validation
+
+
+def _call(**kw):
+    args = dict(q_nope=FAKE, q_rope=FAKE, kv_pool=FAKE, N=100, kv_indptr=FAKE, kv_indices=FAKE,
+                out_cache_loc=FAKE, custom_mask=FAKE, mask_indptr=FAKE, B=1, q_len=9, H=8, scale=0.07,
+                nsplit=4, workspace=0x100000, workspace_bytes=pkg.workspace_size(1, 9, 8, 4), out=FAKE, lse=FAKE,
+                stream=None)
+    args.update(kw)
+    return pkg.attn_raw(**args)
+
+
+@pytest.mark.parametrize("field", ["q_nope", "q_rope", "kv_pool", "kv_indptr", "out_cache_loc", "custom_mask",
+                                   "mask_indptr", "out", "lse"])
+def test_null_pointer_rejected(field):
+    assert _call(**{field: None}) == -1
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(q_len=0), dict(H=0), dict(N=0), dict(N=2**31),
+                                dict(scale=float("inf")), dict(scale=float("nan")), dict(B=1 << 20, H=1 << 11)])
+def test_bad_shape_rejected(kw):
+    assert _call(**kw) == -2
+
+
+@pytest.mark.parametrize("ns", [0, -1, 1025])
+def test_bad_nsplit_rejected(ns):
+    assert _call(nsplit=ns) == -3
+
+
+def test_workspace_rejected():
+    assert _call(workspace=None) == -4
+    assert _call(workspace=0x100010) == -4                      # not 256-byte aligned
+    assert _call(workspace_bytes=pkg.workspace_size(1, 9, 8, 4) - 1) == -4
+
+
+def test_phase_entry_points_validate():
+    ws_bytes = pkg.workspace_size(1, 9, 8, 4)
+    base = (FAKE, FAKE, FAKE, 100, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 9, 8, 0.07, 4, 0x100000, ws_bytes, None)
+    assert pkg.partial_raw(*base[:2], None, *base[3:]) == -1
+    assert pkg.partial_raw(*base[:13], 0, *base[14:]) == -3
+    assert pkg.partial_raw(*base[:15], ws_bytes - 1, None) == -4
+    assert pkg.combine_raw(0x100000, ws_bytes, 1, 9, 8, 4, None, FAKE, None) == -1
+    assert pkg.combine_raw(0x100000, ws_bytes, 1, 9, 8, 5, FAKE, FAKE, None) == -4
+    assert pkg.combine_raw(0x100000, ws_bytes, 0, 9, 8, 4, FAKE, FAKE, None) == -2
