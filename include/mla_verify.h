@@ -47,7 +47,7 @@ extern "C" {
 typedef enum {
     MLA_VERIFY_OK = 0,
     MLA_VERIFY_ERR_NULL = -1,      /* a required pointer is NULL */
-    MLA_VERIFY_ERR_SHAPE = -2,     /* B, q_len, H or N out of range, or scale not finite */
+    MLA_VERIFY_ERR_SHAPE = -2,     /* B, q_len, H or N out of range, or scale not finite and > 0 */
     MLA_VERIFY_ERR_NSPLIT = -3,    /* nsplit outside [1, MLA_VERIFY_MAX_NSPLIT] */
     MLA_VERIFY_ERR_WORKSPACE = -4, /* workspace NULL, misaligned or smaller than required */
     MLA_VERIFY_ERR_LAUNCH = -5     /* the HIP runtime refused a kernel launch */
@@ -91,7 +91,7 @@ const char *mla_verify_status_string(int status);
  *  mask_indptr   int32, at least B entries (a CSR array of B + 1 is accepted; entry B is
  *                never read): start offset of each request's mask.
  *  B, q_len, H   requests, draft tokens per request, query heads; all >= 1.
- *  scale         multiplies the 576-wide dot product before the softmax (finite).
+ *  scale         multiplies the 576-wide dot product before the softmax (finite, > 0).
  *  nsplit        number of contiguous column splits per request, in [1, 1024]. Split s covers
  *                columns [s*chunk, min(L_b, (s+1)*chunk)) with chunk = ceil(L_b / nsplit)
  *                rounded up to a multiple of 32; splits past L_b exit at once.

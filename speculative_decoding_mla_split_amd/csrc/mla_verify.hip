@@ -44,11 +44,13 @@ constexpr int kLoadsPerWave = kRowsPerLoader * kChunks / 64;  // 9 direct-to-LDS
 constexpr int kHalfSteps = (kLatent + kRope) / 32;       // 18 k-steps of 16 per half of the row
 constexpr int kHalfEBlocks = kLatent / 64;               // 8 blocks of 32 output columns per half
 constexpr int kXchgBytes = 64 * 16 * 4;                  // one wave's 32x32 fp32 partial scores
-constexpr int kMaskPairs = 2;                            // token pairs of mask bits prefetched
-constexpr float kRescaleSlack = 8.0f;                    // lazy rescale threshold (log2 units)
+constexpr float kHeadroom = 64.0f;  // scores may exceed a row's reference max by this (log2 units)
+constexpr int kMaskPairs = 2;        // token pairs whose mask bytes ride in the pipeline (H >= 8)
+constexpr int kMetaStages = 4;       // per-wave ring of per-tile metadata (slots + mask bytes)
+constexpr int kMetaBytes = 32 + kMaskPairs * 256;  // 8 slot dwords + 64 mask dwords per token pair
 
 static_assert(kRowsPerLoader * kChunks % 64 == 0, "loader must tile whole wave instructions");
-static_assert(kWaves >= kLoaders, "not enough waves to gather a tile");
+static_assert(kWaves == kLoaders, "every wave gathers a share of each tile");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -65,30 +67,257 @@ __device__ __forceinline__ int swz(int c) { return ((c >> 1) & 3) << 1; }
 
 __device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS reads and writes, then
+// s_barrier. Unlike __syncthreads() it does not drain the vector-memory counter, so direct-to-LDS
+// loads of later tiles stay in flight across it (their completion is awaited explicitly with
+// s_waitcnt vmcnt before the barrier that publishes them). The "memory" clobber keeps the compiler
+// from moving memory accesses across it.
+// Direct-to-LDS loads (LDS address = m0 + size * lane; the probed placement on gfx950, sub-dword
+// sizes zero-extended into a dword). Written as inline asm so the compiler does not pair them with
+// the blanket "wait for every direct-to-LDS load" it would otherwise put in front of each LDS read;
+// the kernel waits for them explicitly with s_waitcnt vmcnt. The compiler sets m0 itself before
+// any instruction that needs it, so overwriting it here is safe.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)reinterpret_cast<uintptr_t>((lds_void*)p));
+}
+__device__ __forceinline__ void dma_b128(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_b32(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_u8(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_ubyte %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 struct Split {
   int b, s, rt;
   bool valid;
 };
 
-// Workgroup id -> (request, split, row tile). Consecutive ids are dispatched round-robin over the
-// 8 XCDs; this mapping gives each XCD a contiguous range of units, so the row tiles of one split
-// (which read the same KV rows) run on the same XCD and share its L2.
+// Workgroup id -> (request, split, row tile). Consecutive workgroup ids are dispatched round-robin
+// over the 8 XCDs. Split sigma = b * nsplit + s goes to XCD sigma % 8 and all its row tiles stay on
+// that XCD (they read the same KV rows, so the re-reads hit its L2), while consecutive splits, and
+// thus every request, are spread evenly over the XCDs. The grid is 8 * ceil(B * nsplit / 8) * n_rt.
 __device__ __forceinline__ Split decode_unit(int B, int nsplit, int n_rt) {
-  const int units = B * nsplit * n_rt;
-  const int per_xcd = (units + 7) / 8;
-  const int u = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  const int xcd = (int)(blockIdx.x % 8), k = (int)(blockIdx.x / 8);
+  const int sigma = xcd + 8 * (k / n_rt);
   Split sp;
-  sp.valid = u < units;
-  sp.rt = u % n_rt;
-  sp.s = (u / n_rt) % nsplit;
-  sp.b = u / (n_rt * nsplit);
+  sp.valid = sigma < B * nsplit;
+  sp.rt = k % n_rt;
+  sp.s = sigma % nsplit;
+  sp.b = sigma / nsplit;
   return sp;
+}
+
+// Per-wave constants of the partial kernel (request/split bounds, lane roles, LDS offsets).
+struct Ctx {
+  size_t mask_base;
+  int N, b, q_len, kv_start, P, L, c_end;
+  int lane, g, hf;
+  int loader_row0;
+  int tok_first, tok_last, my_pair, my_half, n_tok_pairs;
+  float scale_log2;
+  int k_base, k_swz, v_off0, v_off1;
+};
+
+// Direct-to-LDS loads of one tile's metadata into a wave's ring stage m: the 8 slots of the rows
+// this wave gathers (lanes 0-7, dword loads land at m + 4*lane) and, per token pair, one mask byte
+// per lane (lanes 0-31: token tok_first + 2tp, column tile_c0 + lane; lanes 32-63: the next token;
+// byte loads land zero-extended at m + 32 + 256tp + 4*lane). Addresses are clamped to valid ones.
+__device__ __forceinline__ void issue_meta(const Ctx& x, const int32_t* kv_indices, const int32_t* out_cache_loc,
+                                           const uint8_t* custom_mask, int tile_c0, uint8_t* m) {
+  if (x.lane < kRowsPerLoader) {
+    const int c = min(tile_c0 + x.loader_row0 + x.lane, x.c_end - 1);
+    const int32_t* src = c < x.P ? kv_indices + x.kv_start + c : out_cache_loc + (size_t)x.b * x.q_len + (c - x.P);
+    dma_b32(src, lds_addr(m));
+  }
+#pragma unroll
+  for (int tp = 0; tp < kMaskPairs; ++tp) {
+    const int t = min(x.tok_first + 2 * tp + x.g, x.tok_last);
+    const int c = min(tile_c0 + (x.lane & 31), x.c_end - 1);
+    dma_u8(custom_mask + x.mask_base + (size_t)t * x.L + c, lds_addr(m + 32 + 256 * tp));
+  }
+}
+
+// The 9 direct-to-LDS loads of this wave's 8 tile rows [loader_row0, loader_row0 + 8) of the tile
+// buffer dst (slots read from the metadata stage).
+// Instruction j covers LDS chunks [64j, 64j+64) of the wave's rows: lane t -> chunk p = 64j+t of
+// row p/72, read from logical chunk (p % 72) ^ swz(p / 72) (swz(8w + rho) == swz(rho)).
+__device__ __forceinline__ void issue_kv(const Ctx& x, const uint8_t* kv_pool, const uint8_t* slots, uint8_t* dst) {
+  const int slotv = *reinterpret_cast<const int*>(slots + 4 * (x.lane & 7));
+#pragma unroll
+  for (int j = 0; j < kLoadsPerWave; ++j) {
+    const int lo = (64 * j) / kChunks;
+    const int boundary = kChunks * (lo + 1) - 64 * j;
+    const int s_lo = __builtin_amdgcn_readlane(slotv, lo);
+    const int s_hi = __builtin_amdgcn_readlane(slotv, lo + 1 < 8 ? lo + 1 : 7);
+    const bool first = x.lane < boundary;
+    const int slot = min(max(first ? s_lo : s_hi, 0), x.N - 1);
+    const int pc = first ? 64 * j + x.lane - kChunks * lo : 64 * j + x.lane - kChunks * (lo + 1);
+    const int off = (pc ^ swz(first ? lo : lo + 1)) * 16;
+    const uint8_t* src = kv_pool + (size_t)(uint32_t)slot * kRowBytes + off;
+    dma_b128(src, lds_addr(dst + x.loader_row0 * kRowBytes + j * 1024));
+  }
+}
+
+// Visibility word of this lane's row for columns tile_c0 .. tile_c0+31 (bit c <-> tile_c0 + c).
+__device__ __forceinline__ uint32_t mask_word(const Ctx& x, const uint8_t* custom_mask, const uint8_t* m, int tile_c0) {
+  uint32_t bits = 0;
+  const bool col_ok = tile_c0 + (x.lane & 31) < x.c_end;
+#pragma unroll
+  for (int tp = 0; tp < kMaskPairs; ++tp) {
+    const int byte_val = *reinterpret_cast<const int*>(m + 32 + 256 * tp + 4 * x.lane);
+    const bool ok = col_ok && x.tok_first + 2 * tp + x.g <= x.tok_last;
+    const uint64_t bal = __ballot(ok && byte_val != 0);
+    const uint32_t word = x.my_half ? (uint32_t)(bal >> 32) : (uint32_t)bal;
+    bits = x.my_pair == tp ? word : bits;
+  }
+  for (int tp = kMaskPairs; tp < x.n_tok_pairs; ++tp) {  // more than 4 tokens per pair (H < 8)
+    const int t = x.tok_first + 2 * tp + x.g;
+    const bool ok = col_ok && t <= x.tok_last;
+    const int byte_val = ok ? custom_mask[x.mask_base + (size_t)t * x.L + tile_c0 + (x.lane & 31)] : 0;
+    const uint64_t bal = __ballot(byte_val != 0);
+    const uint32_t word = x.my_half ? (uint32_t)(bal >> 32) : (uint32_t)bal;
+    bits = x.my_pair == tp ? word : bits;
+  }
+  return bits;
+}
+
+// One 32-column tile for one wave: prefetch (metadata of tile t+3, rows of tile t+2), partial
+// scores of this wave's half of the 576-wide row, score exchange with the partner wave, mask and
+// online softmax on the summed scores, and the PV update of this wave's half of the output.
+// The LDS pointers are restrict-qualified: the buffers written by direct-to-LDS loads here are
+// never the ones read here, which lets the compiler drop its own blanket wait on those loads (the
+// loads a tile needs are awaited explicitly before the barrier that opens its iteration).
+__device__ __forceinline__ void tile_body(const Ctx& x, int tile_c0,
+                                          const uint8_t* __restrict__ kv_pool, const int32_t* __restrict__ kv_indices,
+                                          const int32_t* __restrict__ out_cache_loc,
+                                          const uint8_t* __restrict__ custom_mask, uint8_t* __restrict__ kv_dst, uint8_t* __restrict__ meta_dst,
+                                          const uint8_t* __restrict__ kb, const uint8_t* __restrict__ meta_slots,
+                                          const uint8_t* __restrict__ meta_mask, uint8_t* __restrict__ x_mine,
+                                          const uint8_t* __restrict__ x_other, const bf16x8 (&q)[kHalfSteps],
+                                          f32x16 (&oacc)[kHalfEBlocks], float& m_ref, float& m_seen, float& l_lane,
+                                          bool& over) {
+  issue_meta(x, kv_indices, out_cache_loc, custom_mask, tile_c0 + 3 * kTile, meta_dst);
+  issue_kv(x, kv_pool, meta_slots, kv_dst);
+  const uint32_t bits = mask_word(x, custom_mask, meta_mask, tile_c0);
+
+  // partial scores S^T = K[:, half] . Q[:, half]^T, LDS reads issued in batches of 6. A pair whose
+  // rows are all padding computes on zero queries (finite, never stored): the pairs of a workgroup
+  // move in lock step through the barriers, so skipping would not save time.
+  f32x16 sacc = {};
+  {
+    const uint8_t* krow = kb + x.k_base;
+    // three batches of 6 K fragments, the next batch's reads issued before this batch's MFMAs
+    bf16x8 kf[2][6];
+    auto load_batch = [&](int bt, bf16x8* dst) {
+#pragma unroll
+      for (int j = 0; j < 6; ++j) {
+        const int logical = 36 * x.hf + 2 * (bt + j) + x.g;
+        dst[j] = *reinterpret_cast<const bf16x8*>(krow + ((logical ^ x.k_swz) * 16));
+      }
+    };
+    load_batch(0, kf[0]);
+#pragma unroll
+    for (int bi = 0; bi < kHalfSteps / 6; ++bi) {
+      if (bi + 1 < kHalfSteps / 6) load_batch(6 * (bi + 1), kf[(bi + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 6; ++j) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[bi & 1][j], q[6 * bi + j], sacc, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      *reinterpret_cast<f32x4*>(x_mine + k * 1024) = f32x4{sacc[4 * k], sacc[4 * k + 1], sacc[4 * k + 2], sacc[4 * k + 3]};
+  }
+  lds_barrier();  // both halves of every pair's scores are in LDS
+
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const f32x4 o = *reinterpret_cast<const f32x4*>(x_other + k * 1024);
+    // the same addition order in both waves keeps their softmax states bit-identical
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sacc[4 * k + j] = x.hf ? o[j] + sacc[4 * k + j] : sacc[4 * k + j] + o[j];
+  }
+
+  // mask + softmax numerators against the row's reference max m_ref (base-2 units of the scaled
+  // score). The reference is the max of the first tile with a visible column and then stays fixed,
+  // so the accumulators are never rescaled; a later score above m_ref + kHeadroom raises `over`,
+  // and the kernel then reruns the split with m_ref = the true max m_seen. Element i of sacc is
+  // column 8(i/4) + 4g + i%4 of the tile.
+  // all 32 columns visible for every row of the wave (prefix tiles): no per-element masking
+  const bool full = __all(bits == 0xFFFFFFFFu);
+  float raw = -INFINITY;  // max of the visible raw dot products (scale > 0)
+  if (full) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) raw = fmaxf(raw, sacc[i]);
+  } else {
+    const uint32_t bsh = bits >> (4 * x.g);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sacc[i] = ((bsh >> (8 * (i >> 2) + (i & 3))) & 1u) ? sacc[i] : -INFINITY;
+      raw = fmaxf(raw, sacc[i]);
+    }
+  }
+  raw = fmaxf(raw, __shfl_xor(raw, 32));
+  const float mx = raw * x.scale_log2;
+  m_seen = fmaxf(m_seen, mx);
+  m_ref = m_ref == -INFINITY ? mx : m_ref;
+  over = over || mx > m_ref + kHeadroom;
+  const float base = m_ref == -INFINITY ? 0.0f : m_ref;
+  bf16x8 pb[2];
+  float psum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], x.scale_log2, -base));  // 2^-inf = 0
+    psum += p;
+    pb[i >> 3][i & 7] = (__bf16)p;
+  }
+  l_lane += psum;
+
+  // O^T[e half] += V^T . P^T; k-step kk covers tile columns [16kk, 16kk+16) permuted as
+  // logical k = 8g + j  <->  column 16kk + 4g + j (j < 4), 16kk + 8 + 4g + (j - 4) (j >= 4)
+  // 16 MFMAs (kk, eb) in 4 batches of 4; the next batch's transposed reads are issued first
+  auto load_v = [&](int bi, bf16x8* dst) {
+    const int kk = bi >> 1, eb0 = 4 * (bi & 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int geb = kHalfEBlocks * x.hf + eb0 + j;  // global block of 32 output columns
+      const uint8_t* p0 = kb + ((geb & 1) ? x.v_off1 : x.v_off0) + 128 * (geb >> 1) + 16 * kk * kRowBytes;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 8 * kRowBytes));
+      const bf16x4 lo4 = __builtin_bit_cast(bf16x4, lo), hi4 = __builtin_bit_cast(bf16x4, hi);
+      dst[j] = bf16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+    }
+  };
+  bf16x8 vf[2][4];
+  load_v(0, vf[0]);
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi) {
+    if (bi + 1 < 4) load_v(bi + 1, vf[(bi + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+    const int kk = bi >> 1, eb0 = 4 * (bi & 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      oacc[eb0 + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[bi & 1][j], pb[kk], oacc[eb0 + j], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // Partial kernel. Wave pair p owns 32 query rows; its wave h (0/1) holds the query values of the
 // row half d in [288h, 288h + 288) and the output columns e in [256h, 256h + 256). Per 32-column
 // tile each wave computes the partial scores of its half, the pair swaps them through LDS, both
 // waves run the same online softmax on the summed scores, and each updates its output half.
+//
+// Vector-memory pipeline: everything a tile needs arrives through direct-to-LDS loads, so no loaded
+// register is waited on inside the loop. Per iteration t a wave issues the metadata of tile t+3
+// (1 + kMaskPairs instructions) and then the 9 row loads of tile t+2, whose slots it reads from its
+// metadata ring. Loads retire in order, so "at most 9 outstanding" at the top of iteration t means
+// tile t's rows and tile t+2's metadata have landed while tile t+1's rows may still be in flight.
+// Prefetches past the split read clamped, valid addresses into buffers that are never read.
 __global__ void __launch_bounds__(kWaves * 64, 1)
 verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restrict__ q_rope,
                       const uint8_t* __restrict__ kv_pool, int N,
@@ -100,6 +329,7 @@ verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restric
                       float* __restrict__ ws_acc) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_kv[kBufs * kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t lds_x[kWaves * kXchgBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_meta[kWaves * kMetaStages * kMetaBytes];
 
   const int lane = threadIdx.x & 63;
   const int w = wave_uniform(threadIdx.x >> 6);
@@ -145,196 +375,87 @@ verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restric
     }
   }
 
-  // ---- gather: loader wave w (< 4) loads tile rows [8w, 8w+8); instruction j of the 9 covers LDS
-  // chunks [64j, 64j+64) of those rows, lane t -> chunk p = 64j+t of row p/72, read from logical
-  // chunk (p % 72) ^ swz(p / 72) of that row (swz(8w + rho) == swz(rho)).
-  const bool loader = w < kLoaders;
-  auto load_slot = [&](int tile_c0) -> int {
-    int c = min(tile_c0 + (w % kLoaders) * kRowsPerLoader + (lane & 7), c_end - 1);
-    int slot = c < P ? kv_indices[kv_start + c] : out_cache_loc[(size_t)b * q_len + (c - P)];
-    return min(max(slot, 0), N - 1);
-  };
-  auto issue_kv = [&](int slotv, int buf) {
-    uint8_t* dst = lds_kv + buf * kTileBytes + w * kRowsPerLoader * kRowBytes;
-    int ln = lane;
-    asm volatile("" : "+v"(ln));  // keep the per-lane offsets inside the loop (register pressure)
-#pragma unroll
-    for (int j = 0; j < kLoadsPerWave; ++j) {
-      const int lo = (64 * j) / kChunks;
-      const int boundary = kChunks * (lo + 1) - 64 * j;
-      const int s_lo = __builtin_amdgcn_readlane(slotv, lo);
-      const int s_hi = __builtin_amdgcn_readlane(slotv, lo + 1 < 8 ? lo + 1 : 7);
-      const bool first = ln < boundary;
-      const int slot = first ? s_lo : s_hi;
-      const int pc = first ? 64 * j + ln - kChunks * lo : 64 * j + ln - kChunks * (lo + 1);
-      const int off = (pc ^ swz(first ? lo : lo + 1)) * 16;
-      const uint8_t* src = kv_pool + (size_t)(uint32_t)slot * kRowBytes + off;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + j * 1024), 16, 0, 0);
-    }
-  };
-
-  // ---- tree-mask bits: the pair's rows span tokens [tok_first, tok_last]; one byte load per lane
-  // covers two tokens x 32 columns and a ballot turns it into two 32-bit visibility words.
-  const size_t mask_base = (size_t)mask_indptr[b];
-  const int tok_first = row0 / H;
-  const int tok_last = (min(row0 + kRowsPerPair, R) - 1) / H;
-  const int my_tok = my_row / H;
-  const int my_pair = (my_tok - tok_first) >> 1, my_half = (my_tok - tok_first) & 1;
-  const int n_tok_pairs = pair_has_rows ? (tok_last - tok_first + 2) >> 1 : 0;
-  auto mask_byte = [&](int tile_c0, int tp) -> int {
-    const int t = tok_first + 2 * tp + g;
-    const int c = tile_c0 + (lane & 31);
-    int v = 0;
-    if (t <= tok_last && c < c_end) v = custom_mask[mask_base + (size_t)t * L + c];
-    return v;
-  };
-  auto mask_bits = [&](int byte_val, int tp, uint32_t cur) -> uint32_t {
-    const uint64_t bal = __ballot(byte_val != 0);
-    const uint32_t word = my_half ? (uint32_t)(bal >> 32) : (uint32_t)bal;
-    return my_pair == tp ? word : cur;
-  };
-
-  // ---- online softmax state (per lane: its row; identical in both waves of the pair)
-  f32x16 oacc[kHalfEBlocks];
-#pragma unroll
-  for (int eb = 0; eb < kHalfEBlocks; ++eb) oacc[eb] = f32x16{};
-  float m_ref = -INFINITY;  // reference max in log2 units (may lag the true max by < slack)
-  float l_lane = 0.0f;
-
-  // K-operand reads: lane reads tile row (lane & 31), logical chunk 36 hf + 2ks + g, i.e. physical
-  // chunk 8(ks/4) + 36 hf + ((2(ks%4) + g) ^ swz(row)) (36 hf is a multiple of 4 but not of 8,
-  // so it is added outside the XOR only for hf = 0; hf = 1 handles the odd group below).
-  const int k_row = lane & 31;
+  Ctx x;
+  x.mask_base = (size_t)mask_indptr[b];
+  x.N = N;
+  x.b = b;
+  x.q_len = q_len;
+  x.kv_start = kv_start;
+  x.P = P;
+  x.L = L;
+  x.c_end = c_end;
+  x.lane = lane;
+  x.g = g;
+  x.hf = hf;
+  x.loader_row0 = (w % kLoaders) * kRowsPerLoader;
+  x.tok_first = row0 / H;
+  x.tok_last = pair_has_rows ? (min(row0 + kRowsPerPair, R) - 1) / H : x.tok_first;
+  const int my_tok_ix = min(my_row, R - 1) / H - x.tok_first;
+  x.my_pair = my_tok_ix >> 1;
+  x.my_half = my_tok_ix & 1;
+  x.n_tok_pairs = (x.tok_last - x.tok_first + 2) >> 1;
+  x.scale_log2 = scale_log2;
+  // K-operand reads: lane reads tile row (lane & 31), logical chunk 36hf + 2ks + g, stored at
+  // physical chunk (36hf + 2ks + g) ^ swz(row).
+  x.k_base = (lane & 31) * kRowBytes;
+  x.k_swz = swz(lane & 31);
   // transposed V reads: the 16-lane group G reads tile rows 16kk + 8m + 4(G/2) + (k16/4), m = 0, 1,
   // latent columns 32eb + 16(G%2) + 4(k16%4) .. +3; physical chunk 8(eb/2) + ((4(eb%2) + vc) ^ swz).
-  const int k16 = lane & 15, G = lane >> 4;
-  const int v_row = 4 * (G >> 1) + (k16 >> 2);
-  const int v_chunk = 2 * (G & 1) + ((k16 & 3) >> 1);
-  int v_off[2];
-#pragma unroll
-  for (int par = 0; par < 2; ++par)
-    v_off[par] = v_row * kRowBytes + (((4 * par + v_chunk) ^ swz(v_row)) * 16) + (k16 & 1) * 8;
+  {
+    const int k16 = lane & 15, G = lane >> 4;
+    const int v_row = 4 * (G >> 1) + (k16 >> 2);
+    const int v_chunk = 2 * (G & 1) + ((k16 & 3) >> 1);
+    x.v_off0 = v_row * kRowBytes + ((v_chunk ^ swz(v_row)) * 16) + (k16 & 1) * 8;
+    x.v_off1 = v_row * kRowBytes + (((4 + v_chunk) ^ swz(v_row)) * 16) + (k16 & 1) * 8;
+  }
+  uint8_t* const meta = lds_meta + w * kMetaStages * kMetaBytes;
   uint8_t* const x_mine = lds_x + w * kXchgBytes + lane * 16;
   const uint8_t* const x_other = lds_x + (w ^ 1) * kXchgBytes + lane * 16;
 
   const int ntiles = (c_end - c_begin + kTile - 1) / kTile;
+  f32x16 oacc[kHalfEBlocks];
+  float m_ref = -INFINITY;   // reference max of the row (base-2 units), fixed once set
+  float m_seen = -INFINITY;  // true max of the row over the split
+  float l_lane = 0.0f;
+  __shared__ int lds_over[kWaves];
 
-  // ---- prologue: KV of tiles 0 and 1 in flight, slots of tile 2 and mask bytes of tile 0 loaded
-  int slot_c = 0;
-  int mbyte_cur[kMaskPairs], mbyte_nxt[kMaskPairs];
+  for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-  for (int tp = 0; tp < kMaskPairs; ++tp) mbyte_cur[tp] = tp < n_tok_pairs ? mask_byte(c_begin, tp) : 0;
-  if (loader) {
-    const int slot_a = load_slot(c_begin);
-    const int slot_b = load_slot(c_begin + kTile);
-    issue_kv(slot_a, 0);
-    if (ntiles > 1) issue_kv(slot_b, 1);
-    slot_c = load_slot(c_begin + 2 * kTile);
-  }
+    for (int eb = 0; eb < kHalfEBlocks; ++eb) oacc[eb] = f32x16{};
+    l_lane = 0.0f;
+    bool over = false;
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int tile_c0 = c_begin + t * kTile;
-    // wait until this wave's loads of tile t have landed: only tile t+1's 9 loads may remain
-    if (loader && t + 1 < ntiles) {
-      __builtin_amdgcn_s_waitcnt((kLoadsPerWave & 0xF) | (0x7 << 4) | (0xF << 8));
-    } else {
-      __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+    // ---- prologue: metadata of tiles 0-2, then rows of tiles 0 and 1 in flight
+    issue_meta(x, kv_indices, out_cache_loc, custom_mask, c_begin, meta);
+    issue_meta(x, kv_indices, out_cache_loc, custom_mask, c_begin + kTile, meta + kMetaBytes);
+    issue_meta(x, kv_indices, out_cache_loc, custom_mask, c_begin + 2 * kTile, meta + 2 * kMetaBytes);
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0): query rows and metadata
+#pragma unroll
+    for (int ks = 0; ks < kHalfSteps; ++ks) asm volatile("" ::"v"(q[ks]));  // query rows ready here
+    issue_kv(x, kv_pool, meta, lds_kv);
+    issue_kv(x, kv_pool, meta + kMetaBytes, lds_kv + kTileBytes);
+
+    for (int t = 0; t < ntiles; ++t) {
+      __builtin_amdgcn_s_waitcnt((kLoadsPerWave & 0xF) | (0x7 << 4) | (0xF << 8));  // vmcnt(9)
+      lds_barrier();  // tile t is in LDS; buffer (t+2)%3 and the score exchange are free again
+      tile_body(x, c_begin + t * kTile, kv_pool, kv_indices, out_cache_loc, custom_mask,
+                lds_kv + ((t + 2) % kBufs) * kTileBytes, meta + ((t + 3) % kMetaStages) * kMetaBytes,
+                lds_kv + (t % kBufs) * kTileBytes, meta + ((t + 2) % kMetaStages) * kMetaBytes,
+                meta + (t % kMetaStages) * kMetaBytes, x_mine, x_other, q, oacc, m_ref, m_seen, l_lane, over);
     }
-    __syncthreads();  // tile t is in LDS; buffer (t+2)%3 and the score exchange are free again
+    // the last iterations prefetched rows past the split; let them land before LDS is reused
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0)
 
-    // prefetch: mask bytes of tile t+1, KV rows of tile t+2, slots of tile t+3
+    // a score above its row's reference + headroom anywhere in the workgroup: rerun the split
+    // with every row's reference at its true max (the second pass cannot overflow)
+    if (lane == 0) lds_over[w] = __any(over) ? 1 : 0;
+    lds_barrier();
+    int any_over = 0;
 #pragma unroll
-    for (int tp = 0; tp < kMaskPairs; ++tp)
-      mbyte_nxt[tp] = (tp < n_tok_pairs && t + 1 < ntiles) ? mask_byte(tile_c0 + kTile, tp) : 0;
-    int slot_d = 0;
-    if (loader) {
-      if (t + 2 < ntiles) issue_kv(slot_c, (t + 2) % kBufs);
-      slot_d = load_slot(tile_c0 + 3 * kTile);
-    }
-
-    const uint8_t* kb = lds_kv + (t % kBufs) * kTileBytes;
-    // partial scores S^T = K[:, half] . Q[:, half]^T
-    f32x16 sacc = {};
-    if (pair_has_rows) {
-      const uint8_t* krow = kb + k_row * kRowBytes;
-      const int ksw = swz(k_row);
-#pragma unroll
-      for (int ks = 0; ks < kHalfSteps; ++ks) {
-        const int logical = 36 * hf + 2 * ks + g;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + ((logical ^ ksw) * 16));
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q[ks], sacc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        *reinterpret_cast<f32x4*>(x_mine + k * 1024) = f32x4{sacc[4 * k], sacc[4 * k + 1], sacc[4 * k + 2], sacc[4 * k + 3]};
-    }
-    __syncthreads();  // both halves of every pair's scores are in LDS
-
-    if (pair_has_rows) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const f32x4 o = *reinterpret_cast<const f32x4*>(x_other + k * 1024);
-        // the same addition order in both waves keeps their softmax states bit-identical
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sacc[4 * k + j] = hf ? o[j] + sacc[4 * k + j] : sacc[4 * k + j] + o[j];
-      }
-      // visibility word of this lane's row for the 32 columns of the tile
-      uint32_t bits = 0;
-#pragma unroll
-      for (int tp = 0; tp < kMaskPairs; ++tp) bits = mask_bits(mbyte_cur[tp], tp, bits);
-      for (int tp = kMaskPairs; tp < n_tok_pairs; ++tp) bits = mask_bits(mask_byte(tile_c0, tp), tp, bits);
-
-      // mask + online softmax; element i of sacc is column 8(i/4) + 4g + i%4 of the tile
-      float v[16];
-      float mx = -INFINITY;
-      const uint32_t bsh = bits >> (4 * g);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        v[i] = ((bsh >> (8 * (i >> 2) + (i & 3))) & 1u) ? sacc[i] * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, v[i]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const bool need = mx > m_ref + kRescaleSlack;
-      if (__any(need)) {
-        const float new_ref = need ? mx : m_ref;
-        const float alpha = !need ? 1.0f : (m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_ref - new_ref));
-#pragma unroll
-        for (int eb = 0; eb < kHalfEBlocks; ++eb) oacc[eb] *= alpha;
-        l_lane *= alpha;
-        m_ref = new_ref;
-      }
-      const float base = m_ref == -INFINITY ? 0.0f : m_ref;
-      bf16x8 pb[2];
-      float psum = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(v[i] - base);
-        psum += p;
-        pb[i >> 3][i & 7] = (__bf16)p;
-      }
-      l_lane += psum;
-
-      // O^T[e half] += V^T . P^T; k-step kk covers tile columns [16kk, 16kk+16) permuted as
-      // logical k = 8g + j  <->  column 16kk + 4g + j (j < 4), 16kk + 8 + 4g + (j - 4) (j >= 4)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-        for (int eb = 0; eb < kHalfEBlocks; ++eb) {
-          const int geb = kHalfEBlocks * hf + eb;  // global block of 32 output columns
-          const uint8_t* p0 = kb + v_off[geb & 1] + 128 * (geb >> 1) + 16 * kk * kRowBytes;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 8 * kRowBytes));
-          const bf16x4 lo4 = __builtin_bit_cast(bf16x4, lo), hi4 = __builtin_bit_cast(bf16x4, hi);
-          const bf16x8 a = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-          oacc[eb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk], oacc[eb], 0, 0, 0);
-        }
-      }
-    }
-
-    // rotate the prefetch registers
-#pragma unroll
-    for (int tp = 0; tp < kMaskPairs; ++tp) mbyte_cur[tp] = mbyte_nxt[tp];
-    slot_c = slot_d;
+    for (int k = 0; k < kWaves; ++k) any_over |= lds_over[k];
+    lds_barrier();
+    if (!any_over) break;
+    m_ref = m_seen;
   }
 
   // ---- partial write: (m_ref, l) and this wave's half of the unnormalised accumulator
@@ -424,7 +545,7 @@ extern "C" const char* mla_verify_status_string(int status) {
   switch (status) {
     case MLA_VERIFY_OK: return "ok";
     case MLA_VERIFY_ERR_NULL: return "a required pointer is NULL";
-    case MLA_VERIFY_ERR_SHAPE: return "B, q_len, H or N out of range, or scale not finite";
+    case MLA_VERIFY_ERR_SHAPE: return "B, q_len, H or N out of range, or scale not finite and positive";
     case MLA_VERIFY_ERR_NSPLIT: return "nsplit outside [1, 1024]";
     case MLA_VERIFY_ERR_WORKSPACE: return "workspace NULL, misaligned or too small";
     case MLA_VERIFY_ERR_LAUNCH: return "kernel launch failed";
@@ -460,8 +581,7 @@ int launch_partial(const void* q_nope, const void* q_rope, const void* kv_pool, 
                    const uint8_t* custom_mask, const int32_t* mask_indptr, int B, int q_len, int H,
                    float scale, int nsplit, const Launch& ws, hipStream_t stream) {
   const int n_rt = (ws.R + kRowsPerWG - 1) / kRowsPerWG;
-  const long long units = (long long)B * nsplit * n_rt;
-  const long long grid = (units + 7) / 8 * 8;
+  const long long grid = ((long long)B * nsplit + 7) / 8 * 8 * n_rt;
   if (grid > INT32_MAX) return MLA_VERIFY_ERR_SHAPE;
   const float scale_log2 = scale * 1.44269504088896340736f;
   hipLaunchKernelGGL(verify_partial_kernel, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream,
@@ -492,7 +612,8 @@ extern "C" int mla_verify_attn_partial(const void* q_nope, const void* q_rope, c
                                        int nsplit, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (inputs_null(q_nope, q_rope, kv_pool, kv_indptr, out_cache_loc, custom_mask, mask_indptr))
     return MLA_VERIFY_ERR_NULL;
-  if (!sizes_ok(B, q_len, H) || N < 1 || N > INT32_MAX || !isfinite(scale)) return MLA_VERIFY_ERR_SHAPE;
+  if (!sizes_ok(B, q_len, H) || N < 1 || N > INT32_MAX || !(scale > 0.0f) || !isfinite(scale))
+    return MLA_VERIFY_ERR_SHAPE;
   const int rc = check_common(B, q_len, H, nsplit, workspace, workspace_bytes);
   if (rc != MLA_VERIFY_OK) return rc;
   return launch_partial(q_nope, q_rope, kv_pool, N, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
@@ -516,7 +637,8 @@ extern "C" int mla_verify_attn(const void* q_nope, const void* q_rope, const voi
                                hipStream_t stream) {
   if (inputs_null(q_nope, q_rope, kv_pool, kv_indptr, out_cache_loc, custom_mask, mask_indptr) || !out || !lse)
     return MLA_VERIFY_ERR_NULL;
-  if (!sizes_ok(B, q_len, H) || N < 1 || N > INT32_MAX || !isfinite(scale)) return MLA_VERIFY_ERR_SHAPE;
+  if (!sizes_ok(B, q_len, H) || N < 1 || N > INT32_MAX || !(scale > 0.0f) || !isfinite(scale))
+    return MLA_VERIFY_ERR_SHAPE;
   int rc = check_common(B, q_len, H, nsplit, workspace, workspace_bytes);
   if (rc != MLA_VERIFY_OK) return rc;
   const Launch ws = split_workspace(workspace, B, q_len, H, nsplit);

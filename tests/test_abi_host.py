@@ -63,7 +63,8 @@ def test_null_pointer_rejected(field):
 
 
 @pytest.mark.parametrize("kw", [dict(B=0), dict(q_len=0), dict(H=0), dict(N=0), dict(N=2**31),
-                                dict(scale=float("inf")), dict(scale=float("nan")), dict(B=1 << 20, H=1 << 11)])
+                                dict(scale=float("inf")), dict(scale=float("nan")), dict(scale=0.0),
+                                dict(scale=-0.5), dict(B=1 << 20, H=1 << 11)])
 def test_bad_shape_rejected(kw):
     assert _call(**kw) == -2
 
