@@ -15,8 +15,8 @@ sample of rows of the same workload and scales it to the whole step.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -216,6 +216,40 @@ def roofline_for(wk, part_us):
                 algorithmic_flops=alg["flops"], algorithmic_bytes=alg["partial_bytes"], arithmetic_intensity=ai)
 
 
+KERNEL_SRC = os.path.join(ROOT, "speculative_decoding_mla_split_amd", "csrc", "mla_verify.hip")
+
+
+def kernel_source_sha():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+
+
+def measured_traffic(workload, nsplit):
+    """HBM bytes per partial-kernel launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary,
+    scaled by the same counters' reading for a plain copy of known size; None when there is no
+    summary for this workload or the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_verify_partial_{workload}_ns{nsplit}.json")
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    t = json.load(open(path))
+    if t.get("source_sha256") != kernel_source_sha():
+        return None, "kernel changed since the counters were taken"
+    fetch = t["fetch_kib_per_dispatch"] * 1024 / t["copy_fetch_factor"]
+    write = t["write_kib_per_dispatch"] * 1024 / t["copy_write_factor"]
+    return fetch + write, path
+
+
+def copy_calibration(gib: float, reps: int):
+    """A plain device copy of a known size (for scaling the FETCH_SIZE / WRITE_SIZE counters)."""
+    import torch
+    n = int(gib * (1 << 30))
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": reps}))
+
+
 def step_floor_us(alg):
     return max(alg["step_bytes"] / (HBM_PEAK_GBS * 1e9), alg["flops"] / (MFMA_BF16_PEAK_TFS * 1e12)) * 1e6
 
@@ -232,6 +266,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true", help="skip the 16k/65k configuration sweep")
     ap.add_argument("--parity-rows", type=int, default=48)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -240,6 +276,10 @@ def main():
                                    "kernel here (multi-GPU sharding is a design note, not built)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(1.0, 4)
+        return
 
     import torch
 
@@ -260,6 +300,10 @@ def main():
     alg = wk.alg
     value = alg["kv_bytes"] / (wall * 1e-6) / 1e9
     floor = step_floor_us(alg)
+    roof = roofline_for(wk, part_s["mean"])
+    traffic, traffic_src = measured_traffic(wl.name, nsplit)
+    roof["traffic"] = traffic
+    roof["traffic_source"] = traffic_src
     result = {
         "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": wall / 1e3, "us_per_step": wall, "higher_is_better": True,
@@ -267,7 +311,7 @@ def main():
         "config": {"workload": wl.name, "B": wl.B, "prefixes": list(wl.prefixes), "q_len": wl.q_len, "H": wl.H,
                    "pool_rows": wl.N, "layout": layout, "nsplit": nsplit, "seed": wl.seed,
                    "scale": "1/sqrt(192)", "parallelism": "single GPU"},
-        "roofline": roofline_for(wk, part_s["mean"]),
+        "roofline": roof,
         "kernels_us": {"partial": part_s, "combine": comb_s, "step_events": stats(stepu)},
         "graph_us_per_step": graph_us,
         "step_floor_us": floor, "step_roofline_frac": floor / wall,

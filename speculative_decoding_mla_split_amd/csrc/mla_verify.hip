@@ -37,7 +37,13 @@ constexpr int kWaves = 2 * kPairs;
 constexpr int kRowsPerPair = 32;
 constexpr int kRowsPerWG = kPairs * kRowsPerPair;        // 64
 constexpr int kBufs = 3;                                 // LDS ring depth
-constexpr int kTileBytes = kTile * kRowBytes;            // 36864
+// LDS tile layout. Loader wave w owns tile rows [8w, 8w+8) in region w; a region holds 9 groups
+// (16-byte chunks 8j .. 8j+7 of all its 8 rows, 128 bytes per row), so one direct-to-LDS
+// instruction fills one group. Regions are 9344 bytes apart (9216 + 128): the 128-byte shift
+// puts row c and row c+8 on opposite halves of the 64 LDS banks.
+constexpr int kGroupBytes = 1024;
+constexpr int kRegionBytes = 9 * kGroupBytes + 128;      // 9344
+constexpr int kTileBytes = 4 * kRegionBytes;             // 37376
 constexpr int kLoaders = 4;                              // waves that gather KV rows
 constexpr int kRowsPerLoader = kTile / kLoaders;         // 8
 constexpr int kLoadsPerWave = kRowsPerLoader * kChunks / 64;  // 9 direct-to-LDS loads
@@ -46,7 +52,8 @@ constexpr int kHalfEBlocks = kLatent / 64;               // 8 blocks of 32 outpu
 constexpr int kXchgBytes = 64 * 16 * 4;                  // one wave's 32x32 fp32 partial scores
 constexpr float kHeadroom = 64.0f;  // scores may exceed a row's reference max by this (log2 units)
 constexpr int kMaskPairs = 2;        // token pairs whose mask bytes ride in the pipeline (H >= 8)
-constexpr int kMetaStages = 4;       // per-wave ring of per-tile metadata (slots + mask bytes)
+constexpr int kMetaStages = 8;       // per-wave ring of per-tile metadata (slots + mask bytes)
+constexpr int kMetaLoads = 1 + kMaskPairs;  // direct-to-LDS loads per metadata stage
 constexpr int kMetaBytes = 32 + kMaskPairs * 256;  // 8 slot dwords + 64 mask dwords per token pair
 
 static_assert(kRowsPerLoader * kChunks % 64 == 0, "loader must tile whole wave instructions");
@@ -60,12 +67,17 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// XOR swizzle of the 16-byte chunks of an LDS KV row: chunk k of tile row c is stored at chunk
-// k ^ swz(c). It spreads the 32-row K-operand reads and the 8-row transposed V reads over all
-// LDS banks; the XOR only touches chunk bits 1-2, so a chunk stays inside its aligned group of 8.
-__device__ __forceinline__ int swz(int c) { return ((c >> 1) & 3) << 1; }
+// XOR swizzle inside a group: logical chunk k of tile row c sits in slot (k % 8) ^ swz(c) of group
+// k / 8. Together with the region shift it spreads the 32-row K-operand reads and the 8-row
+// transposed V reads evenly over the LDS banks.
+__host__ __device__ constexpr int swz(int c) { return ((c >> 1) & 3) << 1; }
 
 __device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Byte offset, inside a tile buffer, of logical 16-byte chunk k of tile row c.
+__host__ __device__ constexpr int tile_offset(int c, int k) {
+  return (c / 8) * kRegionBytes + (k / 8) * kGroupBytes + (c % 8) * 128 + (((k % 8) ^ swz(c)) * 16);
+}
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS reads and writes, then
 // s_barrier. Unlike __syncthreads() it does not drain the vector-memory counter, so direct-to-LDS
@@ -85,6 +97,14 @@ __device__ __forceinline__ void dma_b128(const void* g, uint32_t lds) {
 }
 __device__ __forceinline__ void dma_b32(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+// Group j of a loader wave's region: global src + 128j -> LDS lds + 1024j (+ 16 * lane). The
+// immediate offset is added to both addresses, so m0 is set to lds + 896j.
+template <int J>
+__device__ __forceinline__ void dma_group(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2" ::"v"(g),
+               "s"(lds + 896 * J), "i"(128 * J)
+               : "memory", "m0");
 }
 __device__ __forceinline__ void dma_u8(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_ubyte %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
@@ -120,7 +140,7 @@ struct Ctx {
   int loader_row0;
   int tok_first, tok_last, my_pair, my_half, n_tok_pairs;
   float scale_log2;
-  int k_base, k_swz, v_off0, v_off1;
+  int k_off[4], v_off0, v_off1;
 };
 
 // Direct-to-LDS loads of one tile's metadata into a wave's ring stage m: the 8 slots of the rows
@@ -142,25 +162,32 @@ __device__ __forceinline__ void issue_meta(const Ctx& x, const int32_t* kv_indic
   }
 }
 
-// The 9 direct-to-LDS loads of this wave's 8 tile rows [loader_row0, loader_row0 + 8) of the tile
-// buffer dst (slots read from the metadata stage).
-// Instruction j covers LDS chunks [64j, 64j+64) of the wave's rows: lane t -> chunk p = 64j+t of
-// row p/72, read from logical chunk (p % 72) ^ swz(p / 72) (swz(8w + rho) == swz(rho)).
-__device__ __forceinline__ void issue_kv(const Ctx& x, const uint8_t* kv_pool, const uint8_t* slots, uint8_t* dst) {
-  const int slotv = *reinterpret_cast<const int*>(slots + 4 * (x.lane & 7));
-#pragma unroll
-  for (int j = 0; j < kLoadsPerWave; ++j) {
-    const int lo = (64 * j) / kChunks;
-    const int boundary = kChunks * (lo + 1) - 64 * j;
-    const int s_lo = __builtin_amdgcn_readlane(slotv, lo);
-    const int s_hi = __builtin_amdgcn_readlane(slotv, lo + 1 < 8 ? lo + 1 : 7);
-    const bool first = x.lane < boundary;
-    const int slot = min(max(first ? s_lo : s_hi, 0), x.N - 1);
-    const int pc = first ? 64 * j + x.lane - kChunks * lo : 64 * j + x.lane - kChunks * (lo + 1);
-    const int off = (pc ^ swz(first ? lo : lo + 1)) * 16;
-    const uint8_t* src = kv_pool + (size_t)(uint32_t)slot * kRowBytes + off;
-    dma_b128(src, lds_addr(dst + x.loader_row0 * kRowBytes + j * 1024));
+// Row gather of one tile, split so the 9 loads can be interleaved with MFMA work. Lane t serves row
+// t / 8 and slot t % 8 of every group of this wave's region (region loader_row0 / 8 of the tile
+// buffer): group j moves logical chunk 8j + ((t % 8) ^ swz(t / 8)) of that row, so the row address is
+// computed once and the 9 loads differ only by an immediate offset.
+struct KvGather {
+  const uint8_t* src;
+  uint32_t m0;
+};
+__device__ __forceinline__ KvGather kv_gather_setup(const Ctx& x, const uint8_t* kv_pool, const uint8_t* slots,
+                                                    uint8_t* dst) {
+  const int rho = x.lane >> 3, p = x.lane & 7;
+  const int slot = min(max(*reinterpret_cast<const int*>(slots + 4 * rho), 0), x.N - 1);
+  KvGather k;
+  k.src = kv_pool + (size_t)(uint32_t)slot * kRowBytes + ((p ^ swz(rho)) * 16);
+  k.m0 = lds_addr(dst + (x.loader_row0 / 8) * kRegionBytes);
+  return k;
+}
+template <int J0, int J1>
+__device__ __forceinline__ void kv_gather_groups(const KvGather& k) {
+  if constexpr (J0 < J1) {
+    dma_group<J0>(k.src, k.m0);
+    kv_gather_groups<J0 + 1, J1>(k);
   }
+}
+__device__ __forceinline__ void issue_kv(const Ctx& x, const uint8_t* kv_pool, const uint8_t* slots, uint8_t* dst) {
+  kv_gather_groups<0, 9>(kv_gather_setup(x, kv_pool, slots, dst));
 }
 
 // Visibility word of this lane's row for columns tile_c0 .. tile_c0+31 (bit c <-> tile_c0 + c).
@@ -186,7 +213,7 @@ __device__ __forceinline__ uint32_t mask_word(const Ctx& x, const uint8_t* custo
   return bits;
 }
 
-// One 32-column tile for one wave: prefetch (metadata of tile t+3, rows of tile t+2), partial
+// One 32-column tile for one wave: prefetch (rows of tile t+2, metadata of tile t+4), partial
 // scores of this wave's half of the 576-wide row, score exchange with the partner wave, mask and
 // online softmax on the summed scores, and the PV update of this wave's half of the output.
 // The LDS pointers are restrict-qualified: the buffers written by direct-to-LDS loads here are
@@ -201,8 +228,7 @@ __device__ __forceinline__ void tile_body(const Ctx& x, int tile_c0,
                                           const uint8_t* __restrict__ x_other, const bf16x8 (&q)[kHalfSteps],
                                           f32x16 (&oacc)[kHalfEBlocks], float& m_ref, float& m_seen, float& l_lane,
                                           bool& over) {
-  issue_meta(x, kv_indices, out_cache_loc, custom_mask, tile_c0 + 3 * kTile, meta_dst);
-  issue_kv(x, kv_pool, meta_slots, kv_dst);
+  const KvGather gat = kv_gather_setup(x, kv_pool, meta_slots, kv_dst);
   const uint32_t bits = mask_word(x, custom_mask, meta_mask, tile_c0);
 
   // partial scores S^T = K[:, half] . Q[:, half]^T, LDS reads issued in batches of 6. A pair whose
@@ -210,16 +236,19 @@ __device__ __forceinline__ void tile_body(const Ctx& x, int tile_c0,
   // move in lock step through the barriers, so skipping would not save time.
   f32x16 sacc = {};
   {
-    const uint8_t* krow = kb + x.k_base;
-    // three batches of 6 K fragments, the next batch's reads issued before this batch's MFMAs
+    // three batches of 6 K fragments, the next batch's reads issued before this batch's MFMAs;
+    // fragment ks is logical chunk 36hf + 2ks + g of row (lane & 31): k_off[ks % 4] + 1024 (ks / 4)
     bf16x8 kf[2][6];
     auto load_batch = [&](int bt, bf16x8* dst) {
 #pragma unroll
       for (int j = 0; j < 6; ++j) {
-        const int logical = 36 * x.hf + 2 * (bt + j) + x.g;
-        dst[j] = *reinterpret_cast<const bf16x8*>(krow + ((logical ^ x.k_swz) * 16));
+        const int ks = bt + j;
+        dst[j] = *reinterpret_cast<const bf16x8*>(kb + x.k_off[ks % 4] + kGroupBytes * (ks / 4));
       }
     };
+    // the next tiles' loads (rows of tile t+2 in 3 slices, then the metadata of tile t+4) are issued
+    // between the MFMA batches, so the wave never stalls on a full memory queue while the matrix
+    // pipe is idle
     load_batch(0, kf[0]);
 #pragma unroll
     for (int bi = 0; bi < kHalfSteps / 6; ++bi) {
@@ -228,7 +257,12 @@ __device__ __forceinline__ void tile_body(const Ctx& x, int tile_c0,
 #pragma unroll
       for (int j = 0; j < 6; ++j) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[bi & 1][j], q[6 * bi + j], sacc, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
+      if (bi == 0) kv_gather_groups<0, 3>(gat);
+      if (bi == 1) kv_gather_groups<3, 6>(gat);
+      if (bi == 2) kv_gather_groups<6, 9>(gat);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    issue_meta(x, kv_indices, out_cache_loc, custom_mask, tile_c0 + 4 * kTile, meta_dst);
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       *reinterpret_cast<f32x4*>(x_mine + k * 1024) = f32x4{sacc[4 * k], sacc[4 * k + 1], sacc[4 * k + 2], sacc[4 * k + 3]};
@@ -285,12 +319,12 @@ __device__ __forceinline__ void tile_body(const Ctx& x, int tile_c0,
     const int kk = bi >> 1, eb0 = 4 * (bi & 1);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int geb = kHalfEBlocks * x.hf + eb0 + j;  // global block of 32 output columns
-      const uint8_t* p0 = kb + ((geb & 1) ? x.v_off1 : x.v_off0) + 128 * (geb >> 1) + 16 * kk * kRowBytes;
+      const int leb = eb0 + j;  // block of 32 output columns inside this wave's half
+      // rows 16kk + 8m + v_row (regions 2kk + m), latent chunk 4(8hf + leb) + v_chunk
+      const uint8_t* p0 = kb + (leb & 1 ? x.v_off1 : x.v_off0) + 2 * kk * kRegionBytes + kGroupBytes * (leb >> 1);
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 8 * kRowBytes));
-      const bf16x4 lo4 = __builtin_bit_cast(bf16x4, lo), hi4 = __builtin_bit_cast(bf16x4, hi);
-      dst[j] = bf16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + kRegionBytes));
+      dst[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
   };
   bf16x8 vf[2][4];
@@ -313,11 +347,12 @@ __device__ __forceinline__ void tile_body(const Ctx& x, int tile_c0,
 // waves run the same online softmax on the summed scores, and each updates its output half.
 //
 // Vector-memory pipeline: everything a tile needs arrives through direct-to-LDS loads, so no loaded
-// register is waited on inside the loop. Per iteration t a wave issues the metadata of tile t+3
-// (1 + kMaskPairs instructions) and then the 9 row loads of tile t+2, whose slots it reads from its
-// metadata ring. Loads retire in order, so "at most 9 outstanding" at the top of iteration t means
-// tile t's rows and tile t+2's metadata have landed while tile t+1's rows may still be in flight.
-// Prefetches past the split read clamped, valid addresses into buffers that are never read.
+// register is waited on inside the loop. Per iteration t a wave issues the 9 row loads of tile t+2
+// (slots read from its metadata ring, loads interleaved with the score MFMAs) and then the metadata
+// of tile t+4 (kMetaLoads instructions). Loads retire in order, so "at most 12 outstanding" at the
+// top of iteration t means tile t's rows and tile t+2's metadata have landed while tile t+1's rows
+// and tile t+3's metadata may still be in flight. Prefetches past the split read clamped, valid
+// addresses into buffers that are never read.
 __global__ void __launch_bounds__(kWaves * 64, 1)
 verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restrict__ q_rope,
                       const uint8_t* __restrict__ kv_pool, int N,
@@ -395,18 +430,18 @@ verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restric
   x.my_half = my_tok_ix & 1;
   x.n_tok_pairs = (x.tok_last - x.tok_first + 2) >> 1;
   x.scale_log2 = scale_log2;
-  // K-operand reads: lane reads tile row (lane & 31), logical chunk 36hf + 2ks + g, stored at
-  // physical chunk (36hf + 2ks + g) ^ swz(row).
-  x.k_base = (lane & 31) * kRowBytes;
-  x.k_swz = swz(lane & 31);
+  // K-operand reads: lane reads logical chunk 36hf + 2ks + g of tile row (lane & 31)
+#pragma unroll
+  for (int b4 = 0; b4 < 4; ++b4) x.k_off[b4] = tile_offset(lane & 31, 36 * hf + 2 * b4 + g);
   // transposed V reads: the 16-lane group G reads tile rows 16kk + 8m + 4(G/2) + (k16/4), m = 0, 1,
-  // latent columns 32eb + 16(G%2) + 4(k16%4) .. +3; physical chunk 8(eb/2) + ((4(eb%2) + vc) ^ swz).
+  // latent columns 32eb + 16(G%2) + 4(k16%4) .. +3 of block eb = 8hf + leb, i.e. logical chunk
+  // 4eb + vc with vc = 2(G%2) + (k16%4)/2; the hf part (groups 4hf..) is folded into the offsets.
   {
     const int k16 = lane & 15, G = lane >> 4;
     const int v_row = 4 * (G >> 1) + (k16 >> 2);
     const int v_chunk = 2 * (G & 1) + ((k16 & 3) >> 1);
-    x.v_off0 = v_row * kRowBytes + ((v_chunk ^ swz(v_row)) * 16) + (k16 & 1) * 8;
-    x.v_off1 = v_row * kRowBytes + (((4 + v_chunk) ^ swz(v_row)) * 16) + (k16 & 1) * 8;
+    x.v_off0 = tile_offset(v_row, 32 * hf + v_chunk) + (k16 & 1) * 8;
+    x.v_off1 = tile_offset(v_row, 32 * hf + 4 + v_chunk) + (k16 & 1) * 8;
   }
   uint8_t* const meta = lds_meta + w * kMetaStages * kMetaBytes;
   uint8_t* const x_mine = lds_x + w * kXchgBytes + lane * 16;
@@ -425,21 +460,24 @@ verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restric
     l_lane = 0.0f;
     bool over = false;
 
-    // ---- prologue: metadata of tiles 0-2, then rows of tiles 0 and 1 in flight
+    // ---- prologue, laid out like the steady state: ... rows(t+1), meta(t+3), rows(t+2), meta(t+4) ...
     issue_meta(x, kv_indices, out_cache_loc, custom_mask, c_begin, meta);
     issue_meta(x, kv_indices, out_cache_loc, custom_mask, c_begin + kTile, meta + kMetaBytes);
-    issue_meta(x, kv_indices, out_cache_loc, custom_mask, c_begin + 2 * kTile, meta + 2 * kMetaBytes);
     __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0): query rows and metadata
 #pragma unroll
     for (int ks = 0; ks < kHalfSteps; ++ks) asm volatile("" ::"v"(q[ks]));  // query rows ready here
     issue_kv(x, kv_pool, meta, lds_kv);
+    issue_meta(x, kv_indices, out_cache_loc, custom_mask, c_begin + 2 * kTile, meta + 2 * kMetaBytes);
     issue_kv(x, kv_pool, meta + kMetaBytes, lds_kv + kTileBytes);
+    issue_meta(x, kv_indices, out_cache_loc, custom_mask, c_begin + 3 * kTile, meta + 3 * kMetaBytes);
 
     for (int t = 0; t < ntiles; ++t) {
-      __builtin_amdgcn_s_waitcnt((kLoadsPerWave & 0xF) | (0x7 << 4) | (0xF << 8));  // vmcnt(9)
+      // at most rows(t+1) and meta(t+3) outstanding: rows(t) and meta(t+2) have landed
+      static_assert(kLoadsPerWave + kMetaLoads < 16, "vmcnt immediate");
+      __builtin_amdgcn_s_waitcnt(((kLoadsPerWave + kMetaLoads) & 0xF) | (0x7 << 4) | (0xF << 8));
       lds_barrier();  // tile t is in LDS; buffer (t+2)%3 and the score exchange are free again
       tile_body(x, c_begin + t * kTile, kv_pool, kv_indices, out_cache_loc, custom_mask,
-                lds_kv + ((t + 2) % kBufs) * kTileBytes, meta + ((t + 3) % kMetaStages) * kMetaBytes,
+                lds_kv + ((t + 2) % kBufs) * kTileBytes, meta + ((t + 4) % kMetaStages) * kMetaBytes,
                 lds_kv + (t % kBufs) * kTileBytes, meta + ((t + 2) % kMetaStages) * kMetaBytes,
                 meta + (t % kMetaStages) * kMetaBytes, x_mine, x_other, q, oacc, m_ref, m_seen, l_lane, over);
     }
@@ -475,7 +513,8 @@ verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restric
 }
 
 // One wave per query row (b, r): weights w_s = 2^(m_s - M) over the non-empty partials,
-// out = sum w_s acc_s / sum w_s l_s, lse = (M + log2 sum w_s l_s) * ln 2.
+// out = sum w_s acc_s / sum w_s l_s, lse = (M + log2 sum w_s l_s) * ln 2. Lane k owns output
+// columns [8k, 8k+8); the splits are walked 8 at a time with all their loads issued together.
 __global__ void __launch_bounds__(256)
 verify_combine_kernel(const float2* __restrict__ ws_ml, const float* __restrict__ ws_acc, int B, int R,
                       int nsplit, __bf16* __restrict__ out, float* __restrict__ lse) {
@@ -484,33 +523,50 @@ verify_combine_kernel(const float2* __restrict__ ws_ml, const float* __restrict_
   if (row >= (long)B * R) return;
   const long b = row / R, r = row % R;
   const float2* ml = ws_ml + (size_t)b * nsplit * R + r;
+  // M over the splits: lane s reads split s (and s + 64, ...), then a wave max
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml[(size_t)s * R].x);
+  for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, ml[(size_t)s * R].x);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   bf16x8* o = reinterpret_cast<bf16x8*>(out + (size_t)row * kLatent + lane * 8);
   if (M == -INFINITY) {
     *o = bf16x8{};
     if (lane == 0) lse[row] = -INFINITY;
     return;
   }
-  float acc[8] = {};
+  f32x4 acc0 = {}, acc1 = {};
   float den = 0.0f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float2 st = ml[(size_t)s * R];
-    if (st.x == -INFINITY) continue;  // empty or fully masked split: weight 0, accumulator unused
-    const float wgt = exp2f(st.x - M);
-    den += wgt * st.y;
-    const f32x4* src = reinterpret_cast<const f32x4*>(ws_acc + ((size_t)(b * nsplit + s) * R + r) * kLatent + lane * 8);
-    const f32x4 x0 = src[0], x1 = src[1];
+  const float* base = ws_acc + ((size_t)b * nsplit * R + r) * kLatent + lane * 8;
+  const size_t split_stride = (size_t)R * kLatent;
+  constexpr int kU = 8;
+  for (int s0 = 0; s0 < nsplit; s0 += kU) {
+    float wgt[kU];
+    f32x4 x0[kU], x1[kU];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      acc[k] += wgt * x0[k];
-      acc[4 + k] += wgt * x1[k];
+    for (int u = 0; u < kU; ++u) {
+      const int s = s0 + u;
+      const float2 st = s < nsplit ? ml[(size_t)s * R] : make_float2(-INFINITY, 0.0f);
+      // empty or fully masked split: weight 0 and its accumulator is never read
+      const bool live = st.x != -INFINITY;
+      wgt[u] = live ? __builtin_amdgcn_exp2f(st.x - M) : 0.0f;
+      den += live ? wgt[u] * st.y : 0.0f;
+      const f32x4* src = reinterpret_cast<const f32x4*>(base + (size_t)(live ? s : 0) * split_stride);
+      x0[u] = live ? src[0] : f32x4{};
+      x1[u] = live ? src[1] : f32x4{};
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      acc0 += wgt[u] * x0[u];
+      acc1 += wgt[u] * x1[u];
     }
   }
   const float inv = 1.0f / den;
   bf16x8 res;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) res[k] = (__bf16)(acc[k] * inv);
+  for (int k = 0; k < 4; ++k) {
+    res[k] = (__bf16)(acc0[k] * inv);
+    res[4 + k] = (__bf16)(acc1[k] * inv);
+  }
   *o = res;
   if (lane == 0) lse[row] = (M + log2f(den)) * 0.69314718055994530942f;
 }

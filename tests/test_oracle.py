@@ -349,3 +349,13 @@ def test_planted_mistake_is_caught(name, tmp_path):
     caught = rc != 0 or not (np.all(np.isfinite(out)) and _rel(out, np.array(bo)) <= 1e-12
                              and np.abs(lse - np.array(bl)).max() <= 1e-12)
     assert caught, f"mutant {name} passed the brute-force pin"
+
+
+def test_rows_entry_point_matches_full_call():
+    inp = _mk(25, (40, 7), 5, 3)
+    pool = W.full_pool(inp)
+    out, lse = _run(inp, pool)
+    rows = np.array([[0, 0, 0], [1, 4, 2], [0, 3, 1], [1, 0, 0]], np.int32)
+    ro, rl = oracle.attn_rows(*oracle.inputs_args(inp, pool), rows=rows)
+    assert np.array_equal(ro, out[rows[:, 0], rows[:, 1], rows[:, 2]])
+    assert np.array_equal(rl, lse[rows[:, 0], rows[:, 1], rows[:, 2]])
