@@ -7,17 +7,19 @@
 //   verify_partial_kernel  one workgroup per (request, split, 128-row tile). The 576-wide bf16 KV
 //                          rows of the split are gathered through the two index arrays straight
 //                          into LDS with 16-byte direct-to-LDS loads (three-deep ring of 32-row
-//                          tiles), shared by all 128 query rows (4 waves x 32 rows). QK^T and PV
-//                          run on 32x32x16 bf16 MFMA with fp32 accumulation; the mask lookup and
-//                          online softmax happen in registers between the two.
+//                          tiles), shared by all 128 query rows (2 wave pairs x 64 rows). QK^T and
+//                          PV run on 32x32x16 bf16 MFMA with fp32 accumulation; the mask lookup
+//                          and online softmax happen in registers between the two.
 //   verify_combine_kernel  one wave per query row: log-sum-exp combine of the nsplit partials into
 //                          the bf16 output and the fp32 natural-log LSE.
 //
-// Layout conventions of the partial kernel (per wave, 32 query rows r, columns c of one tile):
+// Layout conventions of the partial kernel (per MFMA block of 32 query rows r, columns c of one
+// tile):
 //   S^T[c][r] = K[c][:] . Q[r][:]  (A = K from LDS, B = Q resident in VGPRs)
 //   O^T[e][r] += V^T[e][c] . P^T[c][r]  (A = V^T via ds_read_b64_tr_b16, B = P^T from registers)
-// so each lane holds one query row (lane % 32) for both S^T and O^T, and the softmax statistics and
-// the rescale factor never leave the lane (only the lane pair l, l^32 shares a row).
+// so each lane holds one query row (lane % 32) for both S^T and O^T, and the softmax statistics
+// never leave the lane (only the lane pair l, l^32 shares a row). A wave keeps two such blocks, so
+// every K or V fragment it reads from LDS feeds two MFMAs.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -34,8 +36,9 @@ constexpr int kChunks = kRowBytes / 16;        // 72 sixteen-byte chunks per KV 
 constexpr int kTile = 32;                      // KV columns per LDS tile
 constexpr int kPairs = 2;                      // wave pairs per workgroup
 constexpr int kWaves = 2 * kPairs;
-constexpr int kRowsPerPair = 32;
-constexpr int kRowsPerWG = kPairs * kRowsPerPair;        // 64
+constexpr int kBlockRows = 32;                 // query rows per MFMA block (one lane per row)
+constexpr int kRowsPerPair = 2 * kBlockRows;   // 64: a pair holds two row blocks
+constexpr int kRowsPerWG = kPairs * kRowsPerPair;        // 128
 constexpr int kBufs = 3;                                 // LDS ring depth
 // LDS tile layout. Loader wave w owns tile rows [8w, 8w+8) in region w; a region holds 9 groups
 // (16-byte chunks 8j .. 8j+7 of all its 8 rows, 128 bytes per row), so one direct-to-LDS
@@ -49,15 +52,18 @@ constexpr int kRowsPerLoader = kTile / kLoaders;         // 8
 constexpr int kLoadsPerWave = kRowsPerLoader * kChunks / 64;  // 9 direct-to-LDS loads
 constexpr int kHalfSteps = (kLatent + kRope) / 32;       // 18 k-steps of 16 per half of the row
 constexpr int kHalfEBlocks = kLatent / 64;               // 8 blocks of 32 output columns per half
-constexpr int kXchgBytes = 64 * 16 * 4;                  // one wave's 32x32 fp32 partial scores
+constexpr int kSXchgBytes = 64 * 16 * 4;                 // one 32x32 block of fp32 partial scores
+constexpr int kPXchgBytes = 64 * 16 * 2;                 // one 32x32 block of bf16 probabilities
 constexpr float kHeadroom = 64.0f;  // scores may exceed a row's reference max by this (log2 units)
 constexpr int kMaskPairs = 2;        // token pairs whose mask bytes ride in the pipeline (H >= 8)
 constexpr int kMetaStages = 8;       // per-wave ring of per-tile metadata (slots + mask bytes)
 constexpr int kMetaLoads = 1 + kMaskPairs;  // direct-to-LDS loads per metadata stage
 constexpr int kMetaBytes = 32 + kMaskPairs * 256;  // 8 slot dwords + 64 mask dwords per token pair
+constexpr int kLdsBytes = kBufs * kTileBytes + kWaves * (kSXchgBytes + kPXchgBytes + kMetaStages * kMetaBytes);
 
 static_assert(kRowsPerLoader * kChunks % 64 == 0, "loader must tile whole wave instructions");
 static_assert(kWaves == kLoaders, "every wave gathers a share of each tile");
+static_assert(kLdsBytes + 64 <= 160 * 1024, "LDS budget of one CU");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -213,87 +219,96 @@ __device__ __forceinline__ uint32_t mask_word(const Ctx& x, const uint8_t* custo
   return bits;
 }
 
-// One 32-column tile for one wave: prefetch (rows of tile t+2, metadata of tile t+4), partial
-// scores of this wave's half of the 576-wide row, score exchange with the partner wave, mask and
-// online softmax on the summed scores, and the PV update of this wave's half of the output.
+// One 32-column tile for one wave. Register set 0 of the wave (q[0], oacc[0]) is its own row block
+// (rows 32hf .. 32hf+31 of the pair), set 1 the partner's block; both hold this wave's half hf of
+// the 576-wide query row and of the 512-wide output row.
+//   1. partial scores of both blocks over the half: each K fragment is read from LDS once and feeds
+//      two MFMAs; the loads of later tiles (rows of t+2, metadata of t+4) go out between batches
+//   2. the partner block's partial goes to LDS; after the barrier the partner's partial of the own
+//      block is added (each wave completes the scores of one block)
+//   3. mask + softmax numerators of the own block against its fixed reference max
+//   4. the bf16 probabilities of the own block go to LDS; after the barrier the partner's are read
+//   5. O^T of both blocks over the output half: each V fragment is read once and feeds two MFMAs
 // The LDS pointers are restrict-qualified: the buffers written by direct-to-LDS loads here are
 // never the ones read here, which lets the compiler drop its own blanket wait on those loads (the
 // loads a tile needs are awaited explicitly before the barrier that opens its iteration).
 __device__ __forceinline__ void tile_body(const Ctx& x, int tile_c0,
                                           const uint8_t* __restrict__ kv_pool, const int32_t* __restrict__ kv_indices,
                                           const int32_t* __restrict__ out_cache_loc,
-                                          const uint8_t* __restrict__ custom_mask, uint8_t* __restrict__ kv_dst, uint8_t* __restrict__ meta_dst,
-                                          const uint8_t* __restrict__ kb, const uint8_t* __restrict__ meta_slots,
-                                          const uint8_t* __restrict__ meta_mask, uint8_t* __restrict__ x_mine,
-                                          const uint8_t* __restrict__ x_other, const bf16x8 (&q)[kHalfSteps],
-                                          f32x16 (&oacc)[kHalfEBlocks], float& m_ref, float& m_seen, float& l_lane,
-                                          bool& over) {
+                                          const uint8_t* __restrict__ custom_mask, uint8_t* __restrict__ kv_dst,
+                                          uint8_t* __restrict__ meta_dst, const uint8_t* __restrict__ kb,
+                                          const uint8_t* __restrict__ meta_slots,
+                                          const uint8_t* __restrict__ meta_mask, uint8_t* __restrict__ s_mine,
+                                          const uint8_t* __restrict__ s_other, uint8_t* __restrict__ p_mine,
+                                          const uint8_t* __restrict__ p_other, const bf16x8 (&q)[2][kHalfSteps],
+                                          f32x16 (&oacc)[2][kHalfEBlocks], float& m_ref, float& m_seen,
+                                          float& l_lane, bool& over) {
   const KvGather gat = kv_gather_setup(x, kv_pool, meta_slots, kv_dst);
-  const uint32_t bits = mask_word(x, custom_mask, meta_mask, tile_c0);
 
-  // partial scores S^T = K[:, half] . Q[:, half]^T, LDS reads issued in batches of 6. A pair whose
-  // rows are all padding computes on zero queries (finite, never stored): the pairs of a workgroup
-  // move in lock step through the barriers, so skipping would not save time.
-  f32x16 sacc = {};
+  // 1. S^T = K[:, half] . Q[:, half]^T for the own block (s_own) and the partner's (s_give). Six
+  // batches of 3 K fragments, the next batch's reads issued before this batch's MFMAs; fragment ks
+  // is logical chunk 36hf + 2ks + g of row (lane & 31): k_off[ks % 4] + 1024 (ks / 4).
+  f32x16 s_own = {}, s_give = {};
   {
-    // three batches of 6 K fragments, the next batch's reads issued before this batch's MFMAs;
-    // fragment ks is logical chunk 36hf + 2ks + g of row (lane & 31): k_off[ks % 4] + 1024 (ks / 4)
-    bf16x8 kf[2][6];
-    auto load_batch = [&](int bt, bf16x8* dst) {
+    bf16x8 kf[2][3];
+    auto load_batch = [&](int ks0, bf16x8* dst) {
 #pragma unroll
-      for (int j = 0; j < 6; ++j) {
-        const int ks = bt + j;
+      for (int j = 0; j < 3; ++j) {
+        const int ks = ks0 + j;
         dst[j] = *reinterpret_cast<const bf16x8*>(kb + x.k_off[ks % 4] + kGroupBytes * (ks / 4));
       }
     };
-    // the next tiles' loads (rows of tile t+2 in 3 slices, then the metadata of tile t+4) are issued
-    // between the MFMA batches, so the wave never stalls on a full memory queue while the matrix
-    // pipe is idle
     load_batch(0, kf[0]);
 #pragma unroll
-    for (int bi = 0; bi < kHalfSteps / 6; ++bi) {
-      if (bi + 1 < kHalfSteps / 6) load_batch(6 * (bi + 1), kf[(bi + 1) & 1]);
+    for (int bi = 0; bi < kHalfSteps / 3; ++bi) {
+      if (bi + 1 < kHalfSteps / 3) load_batch(3 * (bi + 1), kf[(bi + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < 6; ++j) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[bi & 1][j], q[6 * bi + j], sacc, 0, 0, 0);
+      for (int j = 0; j < 3; ++j) {
+        s_own = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[bi & 1][j], q[0][3 * bi + j], s_own, 0, 0, 0);
+        s_give = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[bi & 1][j], q[1][3 * bi + j], s_give, 0, 0, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
-      if (bi == 0) kv_gather_groups<0, 3>(gat);
-      if (bi == 1) kv_gather_groups<3, 6>(gat);
-      if (bi == 2) kv_gather_groups<6, 9>(gat);
+      if (bi == 0) kv_gather_groups<0, 2>(gat);
+      if (bi == 1) kv_gather_groups<2, 4>(gat);
+      if (bi == 2) kv_gather_groups<4, 6>(gat);
+      if (bi == 3) kv_gather_groups<6, 8>(gat);
+      if (bi == 4) kv_gather_groups<8, 9>(gat);
+      if (bi == 5) issue_meta(x, kv_indices, out_cache_loc, custom_mask, tile_c0 + 4 * kTile, meta_dst);
       __builtin_amdgcn_sched_barrier(0);
     }
-    issue_meta(x, kv_indices, out_cache_loc, custom_mask, tile_c0 + 4 * kTile, meta_dst);
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      *reinterpret_cast<f32x4*>(x_mine + k * 1024) = f32x4{sacc[4 * k], sacc[4 * k + 1], sacc[4 * k + 2], sacc[4 * k + 3]};
   }
-  lds_barrier();  // both halves of every pair's scores are in LDS
+  const uint32_t bits = mask_word(x, custom_mask, meta_mask, tile_c0);
 
+  // 2. score exchange inside the pair
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    *reinterpret_cast<f32x4*>(s_mine + k * 1024) = f32x4{s_give[4 * k], s_give[4 * k + 1], s_give[4 * k + 2], s_give[4 * k + 3]};
+  lds_barrier();  // every wave's partner-block partial is in LDS
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const f32x4 o = *reinterpret_cast<const f32x4*>(x_other + k * 1024);
-    // the same addition order in both waves keeps their softmax states bit-identical
+    const f32x4 o = *reinterpret_cast<const f32x4*>(s_other + k * 1024);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sacc[4 * k + j] = x.hf ? o[j] + sacc[4 * k + j] : sacc[4 * k + j] + o[j];
+    for (int j = 0; j < 4; ++j) s_own[4 * k + j] += o[j];
   }
 
-  // mask + softmax numerators against the row's reference max m_ref (base-2 units of the scaled
+  // 3. mask + softmax numerators against the row's reference max m_ref (base-2 units of the scaled
   // score). The reference is the max of the first tile with a visible column and then stays fixed,
   // so the accumulators are never rescaled; a later score above m_ref + kHeadroom raises `over`,
-  // and the kernel then reruns the split with m_ref = the true max m_seen. Element i of sacc is
+  // and the kernel then reruns the split with m_ref = the true max m_seen. Element i of s_own is
   // column 8(i/4) + 4g + i%4 of the tile.
-  // all 32 columns visible for every row of the wave (prefix tiles): no per-element masking
+  // all 32 columns visible for every row of the block (prefix tiles): no per-element masking
   const bool full = __all(bits == 0xFFFFFFFFu);
   float raw = -INFINITY;  // max of the visible raw dot products (scale > 0)
   if (full) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) raw = fmaxf(raw, sacc[i]);
+    for (int i = 0; i < 16; ++i) raw = fmaxf(raw, s_own[i]);
   } else {
     const uint32_t bsh = bits >> (4 * x.g);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      sacc[i] = ((bsh >> (8 * (i >> 2) + (i & 3))) & 1u) ? sacc[i] : -INFINITY;
-      raw = fmaxf(raw, sacc[i]);
+      s_own[i] = ((bsh >> (8 * (i >> 2) + (i & 3))) & 1u) ? s_own[i] : -INFINITY;
+      raw = fmaxf(raw, s_own[i]);
     }
   }
   raw = fmaxf(raw, __shfl_xor(raw, 32));
@@ -302,24 +317,33 @@ __device__ __forceinline__ void tile_body(const Ctx& x, int tile_c0,
   m_ref = m_ref == -INFINITY ? mx : m_ref;
   over = over || mx > m_ref + kHeadroom;
   const float base = m_ref == -INFINITY ? 0.0f : m_ref;
-  bf16x8 pb[2];
+  bf16x8 pb_own[2];
   float psum = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], x.scale_log2, -base));  // 2^-inf = 0
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_own[i], x.scale_log2, -base));  // 2^-inf = 0
     psum += p;
-    pb[i >> 3][i & 7] = (__bf16)p;
+    pb_own[i >> 3][i & 7] = (__bf16)p;
   }
   l_lane += psum;
 
-  // O^T[e half] += V^T . P^T; k-step kk covers tile columns [16kk, 16kk+16) permuted as
-  // logical k = 8g + j  <->  column 16kk + 4g + j (j < 4), 16kk + 8 + 4g + (j - 4) (j >= 4)
-  // 16 MFMAs (kk, eb) in 4 batches of 4; the next batch's transposed reads are issued first
-  auto load_v = [&](int bi, bf16x8* dst) {
-    const int kk = bi >> 1, eb0 = 4 * (bi & 1);
+  // 4. probability exchange inside the pair
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int leb = eb0 + j;  // block of 32 output columns inside this wave's half
+  for (int kk = 0; kk < 2; ++kk) *reinterpret_cast<bf16x8*>(p_mine + kk * 1024) = pb_own[kk];
+  lds_barrier();  // every wave's own-block probabilities are in LDS
+  bf16x8 pb_oth[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) pb_oth[kk] = *reinterpret_cast<const bf16x8*>(p_other + kk * 1024);
+
+  // 5. O^T[e half] += V^T . P^T for both blocks; k-step kk covers tile columns [16kk, 16kk+16)
+  // permuted as logical k = 8g + j  <->  column 16kk + 4g + j (j < 4), 16kk + 8 + 4g + (j - 4)
+  // (j >= 4). 16 V fragments (kk, leb) in 8 batches of 2; the next batch's transposed reads are
+  // issued first.
+  auto load_v = [&](int bi, bf16x8* dst) {
+    const int kk = bi >> 2;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int leb = 2 * (bi & 3) + j;  // block of 32 output columns inside this wave's half
       // rows 16kk + 8m + v_row (regions 2kk + m), latent chunk 4(8hf + leb) + v_chunk
       const uint8_t* p0 = kb + (leb & 1 ? x.v_off1 : x.v_off0) + 2 * kk * kRegionBytes + kGroupBytes * (leb >> 1);
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
@@ -327,24 +351,28 @@ __device__ __forceinline__ void tile_body(const Ctx& x, int tile_c0,
       dst[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
   };
-  bf16x8 vf[2][4];
+  bf16x8 vf[2][2];
   load_v(0, vf[0]);
 #pragma unroll
-  for (int bi = 0; bi < 4; ++bi) {
-    if (bi + 1 < 4) load_v(bi + 1, vf[(bi + 1) & 1]);
+  for (int bi = 0; bi < 8; ++bi) {
+    if (bi + 1 < 8) load_v(bi + 1, vf[(bi + 1) & 1]);
     __builtin_amdgcn_sched_barrier(0);
-    const int kk = bi >> 1, eb0 = 4 * (bi & 1);
+    const int kk = bi >> 2;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      oacc[eb0 + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[bi & 1][j], pb[kk], oacc[eb0 + j], 0, 0, 0);
+    for (int j = 0; j < 2; ++j) {
+      const int leb = 2 * (bi & 3) + j;
+      oacc[0][leb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[bi & 1][j], pb_own[kk], oacc[0][leb], 0, 0, 0);
+      oacc[1][leb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[bi & 1][j], pb_oth[kk], oacc[1][leb], 0, 0, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Partial kernel. Wave pair p owns 32 query rows; its wave h (0/1) holds the query values of the
-// row half d in [288h, 288h + 288) and the output columns e in [256h, 256h + 256). Per 32-column
-// tile each wave computes the partial scores of its half, the pair swaps them through LDS, both
-// waves run the same online softmax on the summed scores, and each updates its output half.
+// Partial kernel. Wave pair p owns 64 query rows in two blocks of 32; its wave h (0/1) holds, for
+// both blocks, the query values of the row half d in [288h, 288h + 288) and the output columns
+// e in [256h, 256h + 256), and runs the softmax of block h. Per 32-column tile each wave computes
+// the partial scores of both blocks over its half, the pair swaps the partials and then the
+// probabilities through LDS, and each wave updates its output half of both blocks.
 //
 // Vector-memory pipeline: everything a tile needs arrives through direct-to-LDS loads, so no loaded
 // register is waited on inside the loop. Per iteration t a wave issues the 9 row loads of tile t+2
@@ -363,7 +391,8 @@ verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restric
                       float scale_log2, int nsplit, int n_rt, float2* __restrict__ ws_ml,
                       float* __restrict__ ws_acc) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_kv[kBufs * kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_x[kWaves * kXchgBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_s[kWaves * kSXchgBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_p[kWaves * kPXchgBytes];
   __shared__ __attribute__((aligned(16))) uint8_t lds_meta[kWaves * kMetaStages * kMetaBytes];
 
   const int lane = threadIdx.x & 63;
@@ -384,29 +413,32 @@ verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restric
   const int c_end = min(L, c_begin + chunk);
 
   const int g = lane >> 5;  // k-group of the MFMA operands
-  const int row0 = sp.rt * kRowsPerWG + pr_id * kRowsPerPair;
-  const int my_row = row0 + (lane & 31);
-  const bool row_ok = my_row < R;
+  const int pair_row0 = sp.rt * kRowsPerWG + pr_id * kRowsPerPair;
+  // register set i of this wave holds row block i ^ hf of the pair: set 0 is the own block
+  auto set_row = [&](int i) { return pair_row0 + kBlockRows * (i ^ hf) + (lane & 31); };
+  const int own_row0 = pair_row0 + kBlockRows * hf;
+  const int own_row = set_row(0);
   const size_t part = ((size_t)b * nsplit + s) * R;
 
   if (c_begin >= c_end) {
-    if (row_ok && g == 0 && hf == 0) ws_ml[part + my_row] = make_float2(-INFINITY, 0.0f);
+    if (own_row < R && g == 0) ws_ml[part + own_row] = make_float2(-INFINITY, 0.0f);
     return;
   }
-  const bool pair_has_rows = row0 < R;
 
-  // ---- this wave's half of the query row as MFMA B operands: k-step ks holds
+  // ---- this wave's half of both blocks' query rows as MFMA B operands: k-step ks of set i holds
   // Q[row][288 hf + 16 ks + 8 g .. +8] (rows past R load row R-1 and are zeroed)
-  bf16x8 q[kHalfSteps];
-  {
-    const int q_row = min(my_row, R - 1);
+  bf16x8 q[2][kHalfSteps];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = set_row(i);
+    const int q_row = min(row, R - 1);
     const bf16x8* qn = reinterpret_cast<const bf16x8*>(q_nope + ((size_t)b * R + q_row) * kLatent);
     const bf16x8* qr = reinterpret_cast<const bf16x8*>(q_rope + ((size_t)b * R + q_row) * kRope);
 #pragma unroll
     for (int ks = 0; ks < kHalfSteps; ++ks) {
       const int chunk8 = 36 * hf + 2 * ks + g;  // 8-value chunk of the 576-wide row
       const bf16x8 v = chunk8 < kLatent / 8 ? qn[chunk8] : qr[chunk8 - kLatent / 8];
-      q[ks] = row_ok ? v : bf16x8{};
+      q[i][ks] = row < R ? v : bf16x8{};
     }
   }
 
@@ -423,9 +455,10 @@ verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restric
   x.g = g;
   x.hf = hf;
   x.loader_row0 = (w % kLoaders) * kRowsPerLoader;
-  x.tok_first = row0 / H;
-  x.tok_last = pair_has_rows ? (min(row0 + kRowsPerPair, R) - 1) / H : x.tok_first;
-  const int my_tok_ix = min(my_row, R - 1) / H - x.tok_first;
+  // tokens of the own block's rows (a block past R uses the last token: valid, never stored)
+  x.tok_first = min(own_row0, R - 1) / H;
+  x.tok_last = (min(own_row0 + kBlockRows, R) - 1) / H;
+  const int my_tok_ix = min(own_row, R - 1) / H - x.tok_first;
   x.my_pair = my_tok_ix >> 1;
   x.my_half = my_tok_ix & 1;
   x.n_tok_pairs = (x.tok_last - x.tok_first + 2) >> 1;
@@ -444,19 +477,23 @@ verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restric
     x.v_off1 = tile_offset(v_row, 32 * hf + 4 + v_chunk) + (k16 & 1) * 8;
   }
   uint8_t* const meta = lds_meta + w * kMetaStages * kMetaBytes;
-  uint8_t* const x_mine = lds_x + w * kXchgBytes + lane * 16;
-  const uint8_t* const x_other = lds_x + (w ^ 1) * kXchgBytes + lane * 16;
+  uint8_t* const s_mine = lds_s + w * kSXchgBytes + lane * 16;
+  const uint8_t* const s_other = lds_s + (w ^ 1) * kSXchgBytes + lane * 16;
+  uint8_t* const p_mine = lds_p + w * kPXchgBytes + lane * 16;
+  const uint8_t* const p_other = lds_p + (w ^ 1) * kPXchgBytes + lane * 16;
 
   const int ntiles = (c_end - c_begin + kTile - 1) / kTile;
-  f32x16 oacc[kHalfEBlocks];
-  float m_ref = -INFINITY;   // reference max of the row (base-2 units), fixed once set
-  float m_seen = -INFINITY;  // true max of the row over the split
+  f32x16 oacc[2][kHalfEBlocks];
+  float m_ref = -INFINITY;   // reference max of the own row (base-2 units), fixed once set
+  float m_seen = -INFINITY;  // true max of the own row over the split
   float l_lane = 0.0f;
   __shared__ int lds_over[kWaves];
 
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int eb = 0; eb < kHalfEBlocks; ++eb) oacc[eb] = f32x16{};
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int eb = 0; eb < kHalfEBlocks; ++eb) oacc[i][eb] = f32x16{};
     l_lane = 0.0f;
     bool over = false;
 
@@ -465,7 +502,9 @@ verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restric
     issue_meta(x, kv_indices, out_cache_loc, custom_mask, c_begin + kTile, meta + kMetaBytes);
     __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0): query rows and metadata
 #pragma unroll
-    for (int ks = 0; ks < kHalfSteps; ++ks) asm volatile("" ::"v"(q[ks]));  // query rows ready here
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int ks = 0; ks < kHalfSteps; ++ks) asm volatile("" ::"v"(q[i][ks]));  // query rows ready here
     issue_kv(x, kv_pool, meta, lds_kv);
     issue_meta(x, kv_indices, out_cache_loc, custom_mask, c_begin + 2 * kTile, meta + 2 * kMetaBytes);
     issue_kv(x, kv_pool, meta + kMetaBytes, lds_kv + kTileBytes);
@@ -475,11 +514,12 @@ verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restric
       // at most rows(t+1) and meta(t+3) outstanding: rows(t) and meta(t+2) have landed
       static_assert(kLoadsPerWave + kMetaLoads < 16, "vmcnt immediate");
       __builtin_amdgcn_s_waitcnt(((kLoadsPerWave + kMetaLoads) & 0xF) | (0x7 << 4) | (0xF << 8));
-      lds_barrier();  // tile t is in LDS; buffer (t+2)%3 and the score exchange are free again
+      lds_barrier();  // tile t is in LDS; buffer (t+2)%3 and the exchange slots are free again
       tile_body(x, c_begin + t * kTile, kv_pool, kv_indices, out_cache_loc, custom_mask,
                 lds_kv + ((t + 2) % kBufs) * kTileBytes, meta + ((t + 4) % kMetaStages) * kMetaBytes,
                 lds_kv + (t % kBufs) * kTileBytes, meta + ((t + 2) % kMetaStages) * kMetaBytes,
-                meta + (t % kMetaStages) * kMetaBytes, x_mine, x_other, q, oacc, m_ref, m_seen, l_lane, over);
+                meta + (t % kMetaStages) * kMetaBytes, s_mine, s_other, p_mine, p_other, q, oacc, m_ref, m_seen,
+                l_lane, over);
     }
     // the last iterations prefetched rows past the split; let them land before LDS is reused
     __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0)
@@ -496,20 +536,25 @@ verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restric
     m_ref = m_seen;
   }
 
-  // ---- partial write: (m_ref, l) and this wave's half of the unnormalised accumulator
+  // ---- partial write: (m_ref, l) of the own block and this wave's half of both blocks'
+  // unnormalised accumulators
   const float l_row = l_lane + __shfl_xor(l_lane, 32);
-  if (row_ok) {
-    float* dst = ws_acc + (part + my_row) * kLatent + 256 * hf;
 #pragma unroll
-    for (int eb = 0; eb < kHalfEBlocks; ++eb) {
+  for (int i = 0; i < 2; ++i) {
+    const int row = set_row(i);
+    if (row < R) {
+      float* dst = ws_acc + (part + row) * kLatent + 256 * hf;
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const f32x4 val = {oacc[eb][4 * a], oacc[eb][4 * a + 1], oacc[eb][4 * a + 2], oacc[eb][4 * a + 3]};
-        *reinterpret_cast<f32x4*>(dst + 32 * eb + 8 * a + 4 * g) = val;
+      for (int eb = 0; eb < kHalfEBlocks; ++eb) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const f32x4 val = {oacc[i][eb][4 * a], oacc[i][eb][4 * a + 1], oacc[i][eb][4 * a + 2], oacc[i][eb][4 * a + 3]};
+          *reinterpret_cast<f32x4*>(dst + 32 * eb + 8 * a + 4 * g) = val;
+        }
       }
     }
-    if (g == 0 && hf == 0) ws_ml[part + my_row] = make_float2(m_ref, l_row);
   }
+  if (own_row < R && g == 0) ws_ml[part + own_row] = make_float2(m_ref, l_row);
 }
 
 // One wave per query row (b, r): weights w_s = 2^(m_s - M) over the non-empty partials,
