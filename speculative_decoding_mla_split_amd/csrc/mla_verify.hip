@@ -55,10 +55,15 @@ constexpr int kHalfEBlocks = kLatent / 64;               // 8 blocks of 32 outpu
 constexpr int kSXchgBytes = 64 * 16 * 4;                 // one 32x32 block of fp32 partial scores
 constexpr int kPXchgBytes = 64 * 16 * 2;                 // one 32x32 block of bf16 probabilities
 constexpr float kHeadroom = 64.0f;  // scores may exceed a row's reference max by this (log2 units)
-constexpr int kMaskPairs = 2;        // token pairs whose mask bytes ride in the pipeline (H >= 8)
-constexpr int kMetaStages = 8;       // per-wave ring of per-tile metadata (slots + mask bytes)
-constexpr int kMetaLoads = 1 + kMaskPairs;  // direct-to-LDS loads per metadata stage
-constexpr int kMetaBytes = 32 + kMaskPairs * 256;  // 8 slot dwords + 64 mask dwords per token pair
+// Per-tile metadata of one wave, all through byte-granular direct-to-LDS loads (each byte lands
+// zero-extended in its own dword): load 0 carries the 4 bytes of each of the 8 slot indices of the
+// rows this wave gathers (lanes 0-31) and the 32 mask bytes of the first token of the wave's row
+// block (lanes 32-63); extra load k carries two more tokens (1 + 2k, 2 + 2k). A 32-row block
+// spans 1 token for H >= 32, so most configurations need a single metadata load per tile.
+constexpr int kMetaExtra = 2;                    // extra mask loads at most (block tokens <= 5)
+constexpr int kMetaTokens = 1 + 2 * kMetaExtra;  // block tokens whose mask bytes ride in LDS
+constexpr int kMetaBytes = 256 * (1 + kMetaExtra);
+constexpr int kMetaStages = 8;                   // per-wave ring of per-tile metadata
 constexpr int kLdsBytes = kBufs * kTileBytes + kWaves * (kSXchgBytes + kPXchgBytes + kMetaStages * kMetaBytes);
 
 static_assert(kRowsPerLoader * kChunks % 64 == 0, "loader must tile whole wave instructions");
@@ -118,6 +123,19 @@ __device__ __forceinline__ void dma_u8(const void* g, uint32_t lds) {
 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Row max / row sum over the lane pair (l, l ^ 32) through v_permlane32_swap, without an LDS round
+// trip. The swap exchanges one wave half of its two operands with the other, so afterwards every
+// lane holds its own value and its partner's, one in each result; max and (commutative) addition
+// of the two give the same bits in both lanes of the pair.
+__device__ __forceinline__ float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 struct Split {
   int b, s, rt;
   bool valid;
@@ -145,28 +163,40 @@ struct Ctx {
   int lane, g, hf;
   int loader_row0;
   int tok_first, tok_last, my_pair, my_half, n_tok_pairs;
+  int n_meta;  // metadata loads per tile of this wave: 1 + extra mask loads (wave-uniform)
   float scale_log2;
   int k_off[4], v_off0, v_off1;
 };
 
-// Direct-to-LDS loads of one tile's metadata into a wave's ring stage m: the 8 slots of the rows
-// this wave gathers (lanes 0-7, dword loads land at m + 4*lane) and, per token pair, one mask byte
-// per lane (lanes 0-31: token tok_first + 2tp, column tile_c0 + lane; lanes 32-63: the next token;
-// byte loads land zero-extended at m + 32 + 256tp + 4*lane). Addresses are clamped to valid ones.
-__device__ __forceinline__ void issue_meta(const Ctx& x, const int32_t* kv_indices, const int32_t* out_cache_loc,
-                                           const uint8_t* custom_mask, int tile_c0, uint8_t* m) {
-  if (x.lane < kRowsPerLoader) {
-    const int c = min(tile_c0 + x.loader_row0 + x.lane, x.c_end - 1);
-    const int32_t* src = c < x.P ? kv_indices + x.kv_start + c : out_cache_loc + (size_t)x.b * x.q_len + (c - x.P);
-    dma_b32(src, lds_addr(m));
-  }
-#pragma unroll
-  for (int tp = 0; tp < kMaskPairs; ++tp) {
-    const int t = min(x.tok_first + 2 * tp + x.g, x.tok_last);
-    const int c = min(tile_c0 + (x.lane & 31), x.c_end - 1);
-    dma_u8(custom_mask + x.mask_base + (size_t)t * x.L + c, lds_addr(m + 32 + 256 * tp));
+// Metadata loads of one tile into a wave's ring stage m (x.n_meta instructions; PART > 0 is a no-op
+// beyond that). Token i of the block lands at m + 128(i + 1) + 4c for column tile_c0 + c; byte j
+// of the slot of gather row r at m + 16r + 4j. Addresses are clamped to valid ones.
+template <int PART>
+__device__ __forceinline__ void issue_meta_part(const Ctx& x, const int32_t* kv_indices, const int32_t* out_cache_loc,
+                                                const uint8_t* custom_mask, int tile_c0, uint8_t* m) {
+  static_assert(PART >= 0 && PART <= kMetaExtra, "metadata part");
+  const int c = min(tile_c0 + (x.lane & 31), x.c_end - 1);
+  const uint8_t* mask_row = custom_mask + x.mask_base + c;
+  if constexpr (PART == 0) {
+    const int cr = min(tile_c0 + x.loader_row0 + ((x.lane & 31) >> 2), x.c_end - 1);
+    const int32_t* slot = cr < x.P ? kv_indices + x.kv_start + cr : out_cache_loc + (size_t)x.b * x.q_len + (cr - x.P);
+    const uint8_t* src = x.g ? mask_row + (size_t)x.tok_first * x.L
+                             : reinterpret_cast<const uint8_t*>(slot) + (x.lane & 3);
+    dma_u8(src, lds_addr(m));
+  } else {
+    if (PART <= x.n_meta - 1) {
+      const int t = min(x.tok_first + 2 * PART - 1 + x.g, x.tok_last);
+      dma_u8(mask_row + (size_t)t * x.L, lds_addr(m + 256 * PART));
+    }
   }
 }
+__device__ __forceinline__ void issue_meta(const Ctx& x, const int32_t* kv_indices, const int32_t* out_cache_loc,
+                                           const uint8_t* custom_mask, int tile_c0, uint8_t* m) {
+  issue_meta_part<0>(x, kv_indices, out_cache_loc, custom_mask, tile_c0, m);
+  issue_meta_part<1>(x, kv_indices, out_cache_loc, custom_mask, tile_c0, m);
+  issue_meta_part<2>(x, kv_indices, out_cache_loc, custom_mask, tile_c0, m);
+}
+static_assert(kMetaExtra == 2, "issue_meta issues every part");
 
 // Row gather of one tile, split so the 9 loads can be interleaved with MFMA work. Lane t serves row
 // t / 8 and slot t % 8 of every group of this wave's region (region loader_row0 / 8 of the tile
@@ -179,7 +209,9 @@ struct KvGather {
 __device__ __forceinline__ KvGather kv_gather_setup(const Ctx& x, const uint8_t* kv_pool, const uint8_t* slots,
                                                     uint8_t* dst) {
   const int rho = x.lane >> 3, p = x.lane & 7;
-  const int slot = min(max(*reinterpret_cast<const int*>(slots + 4 * rho), 0), x.N - 1);
+  const uint32_t* sb = reinterpret_cast<const uint32_t*>(slots + 16 * rho);  // 4 bytes, one per dword
+  const int raw_slot = (int)(sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24));
+  const int slot = min(max(raw_slot, 0), x.N - 1);
   KvGather k;
   k.src = kv_pool + (size_t)(uint32_t)slot * kRowBytes + ((p ^ swz(rho)) * 16);
   k.m0 = lds_addr(dst + (x.loader_row0 / 8) * kRegionBytes);
@@ -200,107 +232,149 @@ __device__ __forceinline__ void issue_kv(const Ctx& x, const uint8_t* kv_pool, c
 __device__ __forceinline__ uint32_t mask_word(const Ctx& x, const uint8_t* custom_mask, const uint8_t* m, int tile_c0) {
   uint32_t bits = 0;
   const bool col_ok = tile_c0 + (x.lane & 31) < x.c_end;
+  if (x.tok_last - x.tok_first < kMetaTokens) {  // wave-uniform: every token of the block is in LDS
 #pragma unroll
-  for (int tp = 0; tp < kMaskPairs; ++tp) {
-    const int byte_val = *reinterpret_cast<const int*>(m + 32 + 256 * tp + 4 * x.lane);
-    const bool ok = col_ok && x.tok_first + 2 * tp + x.g <= x.tok_last;
-    const uint64_t bal = __ballot(ok && byte_val != 0);
-    const uint32_t word = x.my_half ? (uint32_t)(bal >> 32) : (uint32_t)bal;
-    bits = x.my_pair == tp ? word : bits;
-  }
-  for (int tp = kMaskPairs; tp < x.n_tok_pairs; ++tp) {  // more than 4 tokens per pair (H < 8)
-    const int t = x.tok_first + 2 * tp + x.g;
-    const bool ok = col_ok && t <= x.tok_last;
-    const int byte_val = ok ? custom_mask[x.mask_base + (size_t)t * x.L + tile_c0 + (x.lane & 31)] : 0;
-    const uint64_t bal = __ballot(byte_val != 0);
-    const uint32_t word = x.my_half ? (uint32_t)(bal >> 32) : (uint32_t)bal;
-    bits = x.my_pair == tp ? word : bits;
+    for (int tp = 0; tp < (kMetaTokens + 1) / 2; ++tp) {
+      if (tp < x.n_tok_pairs) {
+        const int i = 2 * tp + x.g;  // token of this lane half within the block
+        const bool ok = col_ok && x.tok_first + i <= x.tok_last;
+        const int byte_val = *reinterpret_cast<const int*>(m + 128 * (min(i, kMetaTokens - 1) + 1) + 4 * (x.lane & 31));
+        const uint64_t bal = __ballot(ok && byte_val != 0);
+        const uint32_t word = x.my_half ? (uint32_t)(bal >> 32) : (uint32_t)bal;
+        bits = x.my_pair == tp ? word : bits;
+      }
+    }
+  } else {  // blocks of more than kMetaTokens tokens (H < 8): read every byte directly
+    for (int tp = 0; tp < x.n_tok_pairs; ++tp) {
+      const int t = x.tok_first + 2 * tp + x.g;
+      const bool ok = col_ok && t <= x.tok_last;
+      const int byte_val = ok ? custom_mask[x.mask_base + (size_t)t * x.L + tile_c0 + (x.lane & 31)] : 0;
+      const uint64_t bal = __ballot(byte_val != 0);
+      const uint32_t word = x.my_half ? (uint32_t)(bal >> 32) : (uint32_t)bal;
+      bits = x.my_pair == tp ? word : bits;
+    }
   }
   return bits;
 }
+
+// Global inputs of the partial kernel that the per-tile steps read.
+struct Glob {
+  const uint8_t* kv_pool;
+  const int32_t* kv_indices;
+  const int32_t* out_cache_loc;
+  const uint8_t* custom_mask;
+};
+
+// LDS areas of one wave: the shared tile ring, its private metadata ring, and its lane's entries in
+// the score and probability exchange slots.
+struct Bufs {
+  uint8_t* kv;
+  uint8_t* meta;
+  uint8_t* s_mine;
+  const uint8_t* s_other;
+  uint8_t* p_mine;
+  const uint8_t* p_other;
+};
 
 // One 32-column tile for one wave. Register set 0 of the wave (q[0], oacc[0]) is its own row block
 // (rows 32hf .. 32hf+31 of the pair), set 1 the partner's block; both hold this wave's half hf of
 // the 576-wide query row and of the 512-wide output row.
 //   1. partial scores of both blocks over the half: each K fragment is read from LDS once and feeds
-//      two MFMAs; the loads of later tiles (rows of t+2, metadata of t+4) go out between batches
+//      two MFMAs
 //   2. the partner block's partial goes to LDS; after the barrier the partner's partial of the own
 //      block is added (each wave completes the scores of one block)
 //   3. mask + softmax numerators of the own block against its fixed reference max
 //   4. the bf16 probabilities of the own block go to LDS; after the barrier the partner's are read
 //   5. O^T of both blocks over the output half: each V fragment is read once and feeds two MFMAs
+// Loads: the step issues the 9 row loads of tile t+2 into ring buffer (t+2) % 3 (its previous
+// tile, t-1, every wave finished before the barrier that opened this step) and the metadata loads
+// of tile t+4, spread evenly over all three phases. A wave keeps only a few vector-memory
+// instructions in flight, and one issued into a full queue stalls the wave, so bunching the loads
+// would idle the matrix pipe; a load has about two steps to land.
 // The LDS pointers are restrict-qualified: the buffers written by direct-to-LDS loads here are
-// never the ones read here, which lets the compiler drop its own blanket wait on those loads (the
-// loads a tile needs are awaited explicitly before the barrier that opens its iteration).
-__device__ __forceinline__ void tile_body(const Ctx& x, int tile_c0,
-                                          const uint8_t* __restrict__ kv_pool, const int32_t* __restrict__ kv_indices,
-                                          const int32_t* __restrict__ out_cache_loc,
-                                          const uint8_t* __restrict__ custom_mask, uint8_t* __restrict__ kv_dst,
-                                          uint8_t* __restrict__ meta_dst, const uint8_t* __restrict__ kb,
-                                          const uint8_t* __restrict__ meta_slots,
-                                          const uint8_t* __restrict__ meta_mask, uint8_t* __restrict__ s_mine,
-                                          const uint8_t* __restrict__ s_other, uint8_t* __restrict__ p_mine,
-                                          const uint8_t* __restrict__ p_other, const bf16x8 (&q)[2][kHalfSteps],
-                                          f32x16 (&oacc)[2][kHalfEBlocks], float& m_ref, float& m_seen,
-                                          float& l_lane, bool& over) {
-  const KvGather gat = kv_gather_setup(x, kv_pool, meta_slots, kv_dst);
+// never the ones read here, which lets the compiler drop its own blanket wait on those loads.
+__device__ __forceinline__ void tile_step(const Ctx& x, int t, int c_begin, const Glob& gl, const Bufs& bf,
+                                          const bf16x8 (&q)[2][kHalfSteps], f32x16 (&oacc)[2][kHalfEBlocks],
+                                          float& m_ref, float& m_seen, float& l_lane, bool& over) {
+  const int tile_c0 = c_begin + t * kTile;
+  // The metadata, mask and gather addresses derive from the lane's role; hiding those inputs behind
+  // an empty asm makes the compiler rebuild the addresses in each step as short-lived values instead
+  // of keeping a dozen 64-bit addresses live across the whole loop.
+  Ctx xm = x;
+  asm volatile("" : "+v"(xm.lane), "+v"(xm.g), "+v"(xm.my_pair), "+v"(xm.my_half));
+  const uint8_t* __restrict__ kb = bf.kv + (t % kBufs) * kTileBytes;
+  const KvGather gat = kv_gather_setup(xm, gl.kv_pool, bf.meta + ((t + 2) % kMetaStages) * kMetaBytes,
+                                       bf.kv + ((t + 2) % kBufs) * kTileBytes);
+  uint8_t* const meta_dst = bf.meta + ((t + 4) % kMetaStages) * kMetaBytes;
+  const int meta_c0 = tile_c0 + 4 * kTile;
+  // load slots: 0-35 follow the score MFMAs, 36-39 the softmax chunks, 40-55 the PV MFMA pairs
+  auto loads = [&](int slot) {
+    switch (slot) {  // slot is a constant after unrolling
+      case 1: dma_group<0>(gat.src, gat.m0); break;
+      case 8: dma_group<1>(gat.src, gat.m0); break;
+      case 15: dma_group<2>(gat.src, gat.m0); break;
+      case 22: dma_group<3>(gat.src, gat.m0); break;
+      case 29: dma_group<4>(gat.src, gat.m0); break;
+      case 36: dma_group<5>(gat.src, gat.m0); break;
+      case 38: dma_group<6>(gat.src, gat.m0); break;
+      case 41: dma_group<7>(gat.src, gat.m0); break;
+      case 45: dma_group<8>(gat.src, gat.m0); break;
+      case 49: issue_meta_part<0>(xm, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, meta_c0, meta_dst); break;
+      case 52: issue_meta_part<1>(xm, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, meta_c0, meta_dst); break;
+      case 54: issue_meta_part<2>(xm, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, meta_c0, meta_dst); break;
+      default: break;
+    }
+  };
 
-  // 1. S^T = K[:, half] . Q[:, half]^T for the own block (s_own) and the partner's (s_give). Six
-  // batches of 3 K fragments, the next batch's reads issued before this batch's MFMAs; fragment ks
-  // is logical chunk 36hf + 2ks + g of row (lane & 31): k_off[ks % 4] + 1024 (ks / 4).
+  // 1. S^T = K[:, half] . Q[:, half]^T for the own block (s_own) and the partner's (s_give), one
+  // k-step at a time; fragment ks is logical chunk 36hf + 2ks + g of row (lane & 31), at
+  // k_off[ks % 4] + 1024 (ks / 4), read kKAhead k-steps ahead.
   f32x16 s_own = {}, s_give = {};
+  uint32_t bits;
   {
-    bf16x8 kf[2][3];
-    auto load_batch = [&](int ks0, bf16x8* dst) {
-#pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        const int ks = ks0 + j;
-        dst[j] = *reinterpret_cast<const bf16x8*>(kb + x.k_off[ks % 4] + kGroupBytes * (ks / 4));
-      }
+    constexpr int kKAhead = 2;
+    bf16x8 kf[kKAhead + 1];
+    auto load_k = [&](int ks) {
+      kf[ks % (kKAhead + 1)] = *reinterpret_cast<const bf16x8*>(kb + x.k_off[ks % 4] + kGroupBytes * (ks / 4));
     };
-    load_batch(0, kf[0]);
 #pragma unroll
-    for (int bi = 0; bi < kHalfSteps / 3; ++bi) {
-      if (bi + 1 < kHalfSteps / 3) load_batch(3 * (bi + 1), kf[(bi + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int ks = 0; ks < kKAhead; ++ks) load_k(ks);
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        s_own = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[bi & 1][j], q[0][3 * bi + j], s_own, 0, 0, 0);
-        s_give = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[bi & 1][j], q[1][3 * bi + j], s_give, 0, 0, 0);
-      }
+    for (int ks = 0; ks < kHalfSteps; ++ks) {
+      if (ks + kKAhead < kHalfSteps) load_k(ks + kKAhead);
       __builtin_amdgcn_sched_barrier(0);
-      if (bi == 0) kv_gather_groups<0, 2>(gat);
-      if (bi == 1) kv_gather_groups<2, 4>(gat);
-      if (bi == 2) kv_gather_groups<4, 6>(gat);
-      if (bi == 3) kv_gather_groups<6, 8>(gat);
-      if (bi == 4) kv_gather_groups<8, 9>(gat);
-      if (bi == 5) issue_meta(x, kv_indices, out_cache_loc, custom_mask, tile_c0 + 4 * kTile, meta_dst);
+      s_own = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks % (kKAhead + 1)], q[0][ks], s_own, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      loads(2 * ks);
+      __builtin_amdgcn_sched_barrier(0);
+      s_give = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks % (kKAhead + 1)], q[1][ks], s_give, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      loads(2 * ks + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
+    bits = mask_word(xm, gl.custom_mask, bf.meta + (t % kMetaStages) * kMetaBytes, tile_c0);
   }
-  const uint32_t bits = mask_word(x, custom_mask, meta_mask, tile_c0);
 
   // 2. score exchange inside the pair
 #pragma unroll
   for (int k = 0; k < 4; ++k)
-    *reinterpret_cast<f32x4*>(s_mine + k * 1024) = f32x4{s_give[4 * k], s_give[4 * k + 1], s_give[4 * k + 2], s_give[4 * k + 3]};
+    *reinterpret_cast<f32x4*>(bf.s_mine + k * 1024) = f32x4{s_give[4 * k], s_give[4 * k + 1], s_give[4 * k + 2], s_give[4 * k + 3]};
   lds_barrier();  // every wave's partner-block partial is in LDS
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const f32x4 o = *reinterpret_cast<const f32x4*>(s_other + k * 1024);
+    const f32x4 o = *reinterpret_cast<const f32x4*>(bf.s_other + k * 1024);
 #pragma unroll
     for (int j = 0; j < 4; ++j) s_own[4 * k + j] += o[j];
   }
+  loads(36);
 
   // 3. mask + softmax numerators against the row's reference max m_ref (base-2 units of the scaled
   // score). The reference is the max of the first tile with a visible column and then stays fixed,
   // so the accumulators are never rescaled; a later score above m_ref + kHeadroom raises `over`,
   // and the kernel then reruns the split with m_ref = the true max m_seen. Element i of s_own is
-  // column 8(i/4) + 4g + i%4 of the tile.
-  // all 32 columns visible for every row of the block (prefix tiles): no per-element masking
-  const bool full = __all(bits == 0xFFFFFFFFu);
+  // column 8(i/4) + 4g + i%4 of the tile; bit c of `bits` marks column c visible for this lane's row.
   float raw = -INFINITY;  // max of the visible raw dot products (scale > 0)
-  if (full) {
+  if (__all(bits == 0xFFFFFFFFu)) {  // every column visible for every row (prefix tiles)
 #pragma unroll
     for (int i = 0; i < 16; ++i) raw = fmaxf(raw, s_own[i]);
   } else {
@@ -311,12 +385,12 @@ __device__ __forceinline__ void tile_body(const Ctx& x, int tile_c0,
       raw = fmaxf(raw, s_own[i]);
     }
   }
-  raw = fmaxf(raw, __shfl_xor(raw, 32));
-  const float mx = raw * x.scale_log2;
+  const float mx = pair_max(raw) * x.scale_log2;
   m_seen = fmaxf(m_seen, mx);
   m_ref = m_ref == -INFINITY ? mx : m_ref;
   over = over || mx > m_ref + kHeadroom;
   const float base = m_ref == -INFINITY ? 0.0f : m_ref;
+  loads(37);
   bf16x8 pb_own[2];
   float psum = 0.0f;
 #pragma unroll
@@ -324,46 +398,48 @@ __device__ __forceinline__ void tile_body(const Ctx& x, int tile_c0,
     const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_own[i], x.scale_log2, -base));  // 2^-inf = 0
     psum += p;
     pb_own[i >> 3][i & 7] = (__bf16)p;
+    if (i == 7) {
+      __builtin_amdgcn_sched_barrier(0);
+      loads(38);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   l_lane += psum;
 
   // 4. probability exchange inside the pair
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) *reinterpret_cast<bf16x8*>(p_mine + kk * 1024) = pb_own[kk];
+  for (int kk = 0; kk < 2; ++kk) *reinterpret_cast<bf16x8*>(bf.p_mine + kk * 1024) = pb_own[kk];
   lds_barrier();  // every wave's own-block probabilities are in LDS
   bf16x8 pb_oth[2];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) pb_oth[kk] = *reinterpret_cast<const bf16x8*>(p_other + kk * 1024);
+  for (int kk = 0; kk < 2; ++kk) pb_oth[kk] = *reinterpret_cast<const bf16x8*>(bf.p_other + kk * 1024);
 
   // 5. O^T[e half] += V^T . P^T for both blocks; k-step kk covers tile columns [16kk, 16kk+16)
   // permuted as logical k = 8g + j  <->  column 16kk + 4g + j (j < 4), 16kk + 8 + 4g + (j - 4)
-  // (j >= 4). 16 V fragments (kk, leb) in 8 batches of 2; the next batch's transposed reads are
-  // issued first.
-  auto load_v = [&](int bi, bf16x8* dst) {
-    const int kk = bi >> 2;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int leb = 2 * (bi & 3) + j;  // block of 32 output columns inside this wave's half
-      // rows 16kk + 8m + v_row (regions 2kk + m), latent chunk 4(8hf + leb) + v_chunk
-      const uint8_t* p0 = kb + (leb & 1 ? x.v_off1 : x.v_off0) + 2 * kk * kRegionBytes + kGroupBytes * (leb >> 1);
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + kRegionBytes));
-      dst[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
+  // (j >= 4). V fragment f = (kk, leb) = (f / 8, f % 8) is read kVAhead fragments ahead with two
+  // transposed reads and feeds the MFMAs of both blocks.
+  constexpr int kVAhead = 2;
+  bf16x8 vf[kVAhead + 1];
+  auto load_v = [&](int f) {
+    const int kk = f >> 3, leb = f & 7;  // leb: block of 32 output columns inside this wave's half
+    // rows 16kk + 8m + v_row (regions 2kk + m), latent chunk 4(8hf + leb) + v_chunk
+    const uint8_t* p0 = kb + (leb & 1 ? x.v_off1 : x.v_off0) + 2 * kk * kRegionBytes + kGroupBytes * (leb >> 1);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + kRegionBytes));
+    vf[f % (kVAhead + 1)] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  bf16x8 vf[2][2];
-  load_v(0, vf[0]);
 #pragma unroll
-  for (int bi = 0; bi < 8; ++bi) {
-    if (bi + 1 < 8) load_v(bi + 1, vf[(bi + 1) & 1]);
+  for (int f = 0; f < kVAhead; ++f) load_v(f);
+#pragma unroll
+  for (int f = 0; f < 2 * kHalfEBlocks; ++f) {
+    if (f + kVAhead < 2 * kHalfEBlocks) load_v(f + kVAhead);
     __builtin_amdgcn_sched_barrier(0);
-    const int kk = bi >> 2;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int leb = 2 * (bi & 3) + j;
-      oacc[0][leb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[bi & 1][j], pb_own[kk], oacc[0][leb], 0, 0, 0);
-      oacc[1][leb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[bi & 1][j], pb_oth[kk], oacc[1][leb], 0, 0, 0);
-    }
+    const int kk = f >> 3, leb = f & 7;
+    oacc[0][leb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[f % (kVAhead + 1)], pb_own[kk], oacc[0][leb], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    oacc[1][leb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[f % (kVAhead + 1)], pb_oth[kk], oacc[1][leb], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    loads(40 + f);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -375,12 +451,10 @@ __device__ __forceinline__ void tile_body(const Ctx& x, int tile_c0,
 // probabilities through LDS, and each wave updates its output half of both blocks.
 //
 // Vector-memory pipeline: everything a tile needs arrives through direct-to-LDS loads, so no loaded
-// register is waited on inside the loop. Per iteration t a wave issues the 9 row loads of tile t+2
-// (slots read from its metadata ring, loads interleaved with the score MFMAs) and then the metadata
-// of tile t+4 (kMetaLoads instructions). Loads retire in order, so "at most 12 outstanding" at the
-// top of iteration t means tile t's rows and tile t+2's metadata have landed while tile t+1's rows
-// and tile t+3's metadata may still be in flight. Prefetches past the split read clamped, valid
-// addresses into buffers that are never read.
+// register is waited on inside the loop. Step t issues the 9 row loads of tile t+2 and the n_meta
+// metadata loads of tile t+4. Loads retire in order, so "at most 9 + n_meta outstanding" at the top
+// of step t means everything issued up to step t-2 (tile t's rows, tile t+2's metadata) has landed.
+// Prefetches past the split read clamped, valid addresses into buffers that are never read.
 __global__ void __launch_bounds__(kWaves * 64, 1)
 verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restrict__ q_rope,
                       const uint8_t* __restrict__ kv_pool, int N,
@@ -462,6 +536,8 @@ verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restric
   x.my_pair = my_tok_ix >> 1;
   x.my_half = my_tok_ix & 1;
   x.n_tok_pairs = (x.tok_last - x.tok_first + 2) >> 1;
+  // metadata loads per tile: the first carries token 0, each extra one two more tokens
+  x.n_meta = 1 + min((x.tok_last - x.tok_first + 1) / 2, kMetaExtra);
   x.scale_log2 = scale_log2;
   // K-operand reads: lane reads logical chunk 36hf + 2ks + g of tile row (lane & 31)
 #pragma unroll
@@ -477,10 +553,10 @@ verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restric
     x.v_off1 = tile_offset(v_row, 32 * hf + 4 + v_chunk) + (k16 & 1) * 8;
   }
   uint8_t* const meta = lds_meta + w * kMetaStages * kMetaBytes;
-  uint8_t* const s_mine = lds_s + w * kSXchgBytes + lane * 16;
-  const uint8_t* const s_other = lds_s + (w ^ 1) * kSXchgBytes + lane * 16;
-  uint8_t* const p_mine = lds_p + w * kPXchgBytes + lane * 16;
-  const uint8_t* const p_other = lds_p + (w ^ 1) * kPXchgBytes + lane * 16;
+  const Bufs bf = {lds_kv, meta,
+                   lds_s + w * kSXchgBytes + lane * 16, lds_s + (w ^ 1) * kSXchgBytes + lane * 16,
+                   lds_p + w * kPXchgBytes + lane * 16, lds_p + (w ^ 1) * kPXchgBytes + lane * 16};
+  const Glob gl = {kv_pool, kv_indices, out_cache_loc, custom_mask};
 
   const int ntiles = (c_end - c_begin + kTile - 1) / kTile;
   f32x16 oacc[2][kHalfEBlocks];
@@ -511,15 +587,16 @@ verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restric
     issue_meta(x, kv_indices, out_cache_loc, custom_mask, c_begin + 3 * kTile, meta + 3 * kMetaBytes);
 
     for (int t = 0; t < ntiles; ++t) {
-      // at most rows(t+1) and meta(t+3) outstanding: rows(t) and meta(t+2) have landed
-      static_assert(kLoadsPerWave + kMetaLoads < 16, "vmcnt immediate");
-      __builtin_amdgcn_s_waitcnt(((kLoadsPerWave + kMetaLoads) & 0xF) | (0x7 << 4) | (0xF << 8));
+      // at most the loads of step t-1 (9 rows + n_meta metadata) outstanding
+      static_assert(kLoadsPerWave + kMetaExtra + 1 < 16, "vmcnt immediate");
+      if (x.n_meta == 1)
+        __builtin_amdgcn_s_waitcnt((kLoadsPerWave + 1) | (0x7 << 4) | (0xF << 8));
+      else if (x.n_meta == 2)
+        __builtin_amdgcn_s_waitcnt((kLoadsPerWave + 2) | (0x7 << 4) | (0xF << 8));
+      else
+        __builtin_amdgcn_s_waitcnt((kLoadsPerWave + 3) | (0x7 << 4) | (0xF << 8));
       lds_barrier();  // tile t is in LDS; buffer (t+2)%3 and the exchange slots are free again
-      tile_body(x, c_begin + t * kTile, kv_pool, kv_indices, out_cache_loc, custom_mask,
-                lds_kv + ((t + 2) % kBufs) * kTileBytes, meta + ((t + 4) % kMetaStages) * kMetaBytes,
-                lds_kv + (t % kBufs) * kTileBytes, meta + ((t + 2) % kMetaStages) * kMetaBytes,
-                meta + (t % kMetaStages) * kMetaBytes, s_mine, s_other, p_mine, p_other, q, oacc, m_ref, m_seen,
-                l_lane, over);
+      tile_step(x, t, c_begin, gl, bf, q, oacc, m_ref, m_seen, l_lane, over);
     }
     // the last iterations prefetched rows past the split; let them land before LDS is reused
     __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0)
@@ -538,7 +615,7 @@ verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restric
 
   // ---- partial write: (m_ref, l) of the own block and this wave's half of both blocks'
   // unnormalised accumulators
-  const float l_row = l_lane + __shfl_xor(l_lane, 32);
+  const float l_row = pair_sum(l_lane);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int row = set_row(i);
