@@ -43,6 +43,9 @@ SHAPES = [
     (8, (33,), 2, 1, 64),          # nsplit far above the length: most splits empty
     (9, (3000, 12), 9, 8, 8),      # ragged split counts
     (10, (31, 32, 33), 3, 5, 1),   # tile-edge lengths
+    (11, (200,), 16, 2, 3),        # 16 tokens per 32-row block: mask bytes read directly
+    (12, (90, 257), 12, 4, 4),     # 8 tokens per block, ragged
+    (13, (300,), 6, 48, 4),        # H = 48: blocks straddle two tokens
 ]
 
 
