@@ -250,6 +250,92 @@ def copy_calibration(gib: float, reps: int):
     print(json.dumps({"copy_bytes_per_launch": n, "launches": reps}))
 
 
+def _event_mean_us(stream, fn, reps, warmup=3):
+    """Mean duration of fn() over reps back-to-back launches, timed with HIP events on `stream`."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def measure_tree_mask(inp, stream, dev, reps=50):
+    """Device tree -> mask builder on the workload's trees: time per call, bytes written, parity."""
+    import numpy as np
+    import torch
+
+    import speculative_decoding_mla_split_amd as pkg
+    parents = torch.from_numpy(np.stack(inp.parents).astype(np.int32)).to(dev)
+    kv_indptr = torch.from_numpy(inp.kv_indptr).to(dev)
+    total = int(inp.mask_indptr[-1])
+    mask = torch.empty(total, dtype=torch.uint8, device=dev)
+    indptr = torch.empty(inp.B + 1, dtype=torch.int32, device=dev)
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    us = _event_mean_us(stream, lambda: pkg.build_tree_mask(parents, kv_indptr, mask, indptr, status, stream=stream),
+                        reps)
+    exact = bool(np.array_equal(mask.cpu().numpy(), inp.custom_mask)
+                 and np.array_equal(indptr.cpu().numpy(), inp.mask_indptr) and int(status.item()) == 0)
+    nbytes = total + 4 * (inp.B + 1) + 4 * parents.numel() + 4 * (inp.B + 1)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"us_per_call": us, "mask_bytes": total, "algorithmic_bytes": nbytes, "achieved_GBs": gbs,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS},
+            "launches_per_call": 2, "bit_exact_vs_generator": exact, "reps": reps}
+
+
+def measure_kv_compact(inp, wl, stream, dev, partial_us_scattered, nsplit, reps=10):
+    """KV compaction of every prefix row into runs past the pool's used rows: time, bandwidth, and the
+    partial kernel's time on the compacted indices next to the scattered ones."""
+    import numpy as np
+    import torch
+
+    import speculative_decoding_mla_split_amd as pkg
+    import workloads as W
+    tot = int(inp.kv_indptr[-1])
+    N = wl.N + tot
+    pool = torch.full((N, 576), W.BF16_NAN, dtype=torch.int16, device=dev)
+    pool[torch.from_numpy(inp.ref_slots.astype(np.int64)).to(dev)] = torch.from_numpy(inp.ref_rows.view(np.int16)).to(dev)
+    pool = pool.view(torch.bfloat16)
+    kv_indptr = torch.from_numpy(inp.kv_indptr).to(dev)
+    kv_indices = torch.from_numpy(inp.kv_indices).to(dev)
+    starts = torch.from_numpy((wl.N + inp.kv_indptr[:-1]).astype(np.int32)).to(dev)
+    new_idx = torch.empty(tot, dtype=torch.int32, device=dev)
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    us = _event_mean_us(stream, lambda: pkg.compact_kv(pool, kv_indptr, kv_indices, starts, new_idx, status,
+                                                        stream=stream), reps, warmup=1)
+    ok = int(status.item()) == 0 and bool(np.array_equal(
+        new_idx.cpu().numpy(), np.concatenate([wl.N + inp.kv_indptr[b] + np.arange(inp.prefixes[b])
+                                               for b in range(inp.B)])))
+    nbytes = 2 * tot * 1152 + 8 * tot
+    gbs = nbytes / (us * 1e-6) / 1e9
+    # the partial kernel over the compacted prefix rows (draft rows stay where they are)
+    ws = torch.empty(pkg.workspace_size(inp.B, inp.q_len, inp.H, nsplit), dtype=torch.uint8, device=dev)
+    q_nope = torch.from_numpy(inp.q_nope.view(np.int16)).to(dev).view(torch.bfloat16)
+    q_rope = torch.from_numpy(inp.q_rope.view(np.int16)).to(dev).view(torch.bfloat16)
+    occ = torch.from_numpy(inp.out_cache_loc).to(dev)
+    cmask = torch.from_numpy(inp.custom_mask).to(dev)
+    mip = torch.from_numpy(inp.mask_indptr).to(dev)
+
+    def part():
+        rc = pkg.partial_raw(q_nope.data_ptr(), q_rope.data_ptr(), pool.data_ptr(), N, kv_indptr.data_ptr(),
+                             new_idx.data_ptr(), occ.data_ptr(), cmask.data_ptr(), mip.data_ptr(), inp.B, inp.q_len,
+                             inp.H, inp.scale, nsplit, ws.data_ptr(), ws.numel(), stream.cuda_stream)
+        assert rc == 0
+    part_us = _event_mean_us(stream, part, 20)
+    return {"us_per_call": us, "rows_moved": tot, "algorithmic_bytes": nbytes, "achieved_GBs": gbs,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS},
+            "indices_exact": ok, "partial_us_scattered": partial_us_scattered, "partial_us_compacted": part_us,
+            "break_even_steps": (us / (partial_us_scattered - part_us)) if partial_us_scattered > part_us else None,
+            "reps": reps}
+
+
 def step_floor_us(alg):
     return max(alg["step_bytes"] / (HBM_PEAK_GBS * 1e9), alg["flops"] / (MFMA_BF16_PEAK_TFS * 1e12)) * 1e6
 
@@ -266,6 +352,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true", help="skip the 16k/65k configuration sweep")
     ap.add_argument("--parity-rows", type=int, default=48)
+    ap.add_argument("--no-next", action="store_true", help="skip the tree-mask and KV-compaction measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -321,6 +408,14 @@ def main():
     main_inp = wk.inp
     del wk
     torch.cuda.empty_cache()
+
+    if not args.no_next:
+        print("[bench] tree mask builder", file=sys.stderr, flush=True)
+        nxt = {"tree_mask": measure_tree_mask(main_inp, stream, dev)}
+        print("[bench] kv compaction", file=sys.stderr, flush=True)
+        nxt["kv_compact"] = measure_kv_compact(main_inp, wl, stream, dev, part_s["mean"], nsplit)
+        result["next_rows"] = nxt
+        torch.cuda.empty_cache()
 
     if not args.no_others:
         others = []

@@ -12,8 +12,10 @@ this module. The HIP library never calls it and shares no code with it.
    Architecture of Capture Safety": raw custom_mask with mask_indptr offsets). The pages time
    this step on the host; they print no mask.
 2. compact_kv: the relocation step the pages designed and deferred ("From Capture Safety to
-   MoE Ceiling", section "Tier 0 Defrag"; "The Decision: Why Tier 1 Defrag Gets Deferred"):
-   copy each request's prefix rows into a contiguous run of slots and rewrite its indices.
+   MoE Ceiling", section "Tier 0 Defrag: The Art of Knowing When to Stop"; "The Art of Knowing
+   When to Stop: Deferring Tier 1 Defrag", section "The Decision: Why Tier 1 Defrag Gets
+   Deferred"): copy each request's prefix rows into a contiguous run of slots and rewrite
+   its indices.
 
 Readings where the pages are silent (listed with the other readings of the pages):
  - parents[b*q_len + i] is the index of draft token i's parent inside request b, -1 for a root.

@@ -47,6 +47,10 @@ def library() -> ctypes.CDLL:
         lib.mla_verify_attn_partial.restype = i32
         lib.mla_verify_attn_combine.argtypes = [vp, sz, i32, i32, i32, i32, vp, vp, vp]
         lib.mla_verify_attn_combine.restype = i32
+        lib.mla_verify_tree_mask.argtypes = [vp, vp, i32, i32, vp, i64, vp, vp, vp]
+        lib.mla_verify_tree_mask.restype = i32
+        lib.mla_verify_kv_compact.argtypes = [vp, i64, vp, vp, vp, i32, vp, vp, vp]
+        lib.mla_verify_kv_compact.restype = i32
         _lib = lib
     return _lib
 
@@ -80,6 +84,22 @@ def combine_raw(workspace, workspace_bytes, B, q_len, H, nsplit, out, lse, strea
     """Direct call of mla_verify_attn_combine with integer device addresses; returns the status."""
     return int(library().mla_verify_attn_combine(workspace, int(workspace_bytes), int(B), int(q_len), int(H),
                                                  int(nsplit), out, lse, stream))
+
+
+def tree_mask_raw(parents, kv_indptr, B, q_len, custom_mask, mask_capacity, mask_indptr, status, stream) -> int:
+    """Direct call of mla_verify_tree_mask with integer device addresses; returns the status."""
+    return int(library().mla_verify_tree_mask(parents, kv_indptr, int(B), int(q_len), custom_mask,
+                                              int(mask_capacity), mask_indptr, status, stream))
+
+
+def kv_compact_raw(kv_pool, N, kv_indptr, kv_indices, dst_start, B, new_kv_indices, status, stream) -> int:
+    """Direct call of mla_verify_kv_compact with integer device addresses; returns the status."""
+    return int(library().mla_verify_kv_compact(kv_pool, int(N), kv_indptr, kv_indices, dst_start, int(B),
+                                               new_kv_indices, status, stream))
+
+
+TREE_BAD_PARENT, TREE_CAPACITY = 1, 2
+COMPACT_BAD_DST, COMPACT_BAD_SRC = 1, 2
 
 
 def _need(cond, msg):
@@ -121,5 +141,59 @@ def verify_attn(q_nope, q_rope, kv_pool, kv_indptr, kv_indices, out_cache_loc, c
                   out_cache_loc.data_ptr(), custom_mask.data_ptr(), mask_indptr.data_ptr(), B, q_len, H, scale,
                   nsplit, workspace.data_ptr(), workspace.numel(), out.data_ptr(), lse.data_ptr(),
                   stream.cuda_stream)
+    if rc != 0:
+        raise MlaVerifyError(rc, status_string(rc))
+
+
+def _dev_i32(name, t):
+    import torch
+    _need(t.dtype == torch.int32 and t.is_cuda and t.is_contiguous(), f"{name} must be a contiguous int32 device tensor")
+
+
+def build_tree_mask(parents, kv_indptr, custom_mask, mask_indptr, status, stream=None) -> None:
+    """Device-built custom_mask + mask_indptr from draft trees (no copies, no host synchronisation).
+
+    parents int32 [B, q_len] (parent index inside the request, -1 for a root), kv_indptr int32 [B+1],
+    custom_mask uint8 (capacity = its numel), mask_indptr int32 [B+1], status int32 [1]
+    (TREE_BAD_PARENT / TREE_CAPACITY bits, read it whenever convenient).
+    """
+    import torch
+
+    _need(parents.dim() == 2, "parents must be [B, q_len]")
+    B, q_len = parents.shape
+    for name, t in (("parents", parents), ("kv_indptr", kv_indptr), ("mask_indptr", mask_indptr),
+                    ("status", status)):
+        _dev_i32(name, t)
+    _need(custom_mask.dtype in (torch.uint8, torch.bool) and custom_mask.is_cuda and custom_mask.is_contiguous(),
+          "custom_mask must be a contiguous uint8/bool device tensor")
+    _need(kv_indptr.numel() >= B + 1 and mask_indptr.numel() >= B + 1 and status.numel() >= 1, "array lengths")
+    if stream is None:
+        stream = torch.cuda.current_stream(parents.device)
+    rc = tree_mask_raw(parents.data_ptr(), kv_indptr.data_ptr(), B, q_len, custom_mask.data_ptr(),
+                       custom_mask.numel(), mask_indptr.data_ptr(), status.data_ptr(), stream.cuda_stream)
+    if rc != 0:
+        raise MlaVerifyError(rc, status_string(rc))
+
+
+def compact_kv(kv_pool, kv_indptr, kv_indices, dst_start, new_kv_indices, status, stream=None) -> None:
+    """Move each request's prefix rows to dst_start[b] + j in place and write the new indices.
+
+    kv_pool bf16 [N, 576] (modified), kv_indptr int32 [B+1], kv_indices int32, dst_start int32 [B],
+    new_kv_indices int32 (same length as kv_indices, not overlapping it), status int32 [1]
+    (COMPACT_BAD_DST / COMPACT_BAD_SRC bits).
+    """
+    import torch
+
+    _need(kv_pool.dim() == 2 and kv_pool.shape[1] == ROW and kv_pool.dtype == torch.bfloat16 and kv_pool.is_cuda
+          and kv_pool.is_contiguous(), "kv_pool must be a contiguous bf16 [N, 576] device tensor")
+    B = dst_start.numel()
+    for name, t in (("kv_indptr", kv_indptr), ("kv_indices", kv_indices), ("dst_start", dst_start),
+                    ("new_kv_indices", new_kv_indices), ("status", status)):
+        _dev_i32(name, t)
+    _need(kv_indptr.numel() >= B + 1 and new_kv_indices.numel() >= kv_indices.numel(), "array lengths")
+    if stream is None:
+        stream = torch.cuda.current_stream(kv_pool.device)
+    rc = kv_compact_raw(kv_pool.data_ptr(), kv_pool.shape[0], kv_indptr.data_ptr(), kv_indices.data_ptr(),
+                        dst_start.data_ptr(), B, new_kv_indices.data_ptr(), status.data_ptr(), stream.cuda_stream)
     if rc != 0:
         raise MlaVerifyError(rc, status_string(rc))

@@ -6,7 +6,7 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "mla_verify.hip")
+SOURCES = [os.path.join(PKG, "csrc", f) for f in ("mla_verify.hip", "tree_mask.hip", "kv_compact.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla_verify.so")
 
@@ -19,10 +19,10 @@ HIPCC_FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
-    """Compile csrc/mla_verify.hip into LIB (always recompiles)."""
+    """Compile the csrc/*.hip sources into LIB (always recompiles)."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, SRC, "-o", tmp]
+    cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, *SOURCES, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr}")

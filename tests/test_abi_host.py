@@ -1,5 +1,6 @@
 """C-ABI checks that need no GPU: symbols, workspace sizing, argument validation before any HIP call."""
 import ctypes
+import glob
 import os
 import re
 
@@ -7,20 +8,23 @@ import pytest
 
 import speculative_decoding_mla_split_amd as pkg
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mla_verify.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mla_verify_\w+)\s*\(", text)))
+    names = set()
+    for h in glob.glob(os.path.join(INCLUDE, "*.h")):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(mla_verify_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
     lib = pkg.library()
     names = _declared_functions()
     assert set(names) == {"mla_verify_attn", "mla_verify_attn_partial", "mla_verify_attn_combine",
-                          "mla_verify_attn_workspace_size", "mla_verify_status_string"}
+                          "mla_verify_attn_workspace_size", "mla_verify_status_string",
+                          "mla_verify_tree_mask", "mla_verify_kv_compact"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -89,3 +93,21 @@ def test_phase_entry_points_validate():
     assert pkg.combine_raw(0x100000, ws_bytes, 1, 9, 8, 4, None, FAKE, None) == -1
     assert pkg.combine_raw(0x100000, ws_bytes, 1, 9, 8, 5, FAKE, FAKE, None) == -4
     assert pkg.combine_raw(0x100000, ws_bytes, 0, 9, 8, 4, FAKE, FAKE, None) == -2
+
+
+def test_tree_mask_validates_before_any_hip_call():
+    ok = dict(parents=FAKE, kv_indptr=FAKE, B=2, q_len=9, custom_mask=FAKE, mask_capacity=1000, mask_indptr=FAKE,
+              status=FAKE, stream=None)
+    for f in ("parents", "kv_indptr", "custom_mask", "mask_indptr", "status"):
+        assert pkg.tree_mask_raw(**{**ok, f: None}) == -1, f
+    for kw in (dict(B=0), dict(B=65536), dict(q_len=0), dict(q_len=4097), dict(mask_capacity=-1)):
+        assert pkg.tree_mask_raw(**{**ok, **kw}) == -2, kw
+
+
+def test_kv_compact_validates_before_any_hip_call():
+    ok = dict(kv_pool=FAKE, N=100, kv_indptr=FAKE, kv_indices=FAKE, dst_start=FAKE, B=2, new_kv_indices=FAKE,
+              status=FAKE, stream=None)
+    for f in ("kv_pool", "kv_indptr", "kv_indices", "dst_start", "new_kv_indices", "status"):
+        assert pkg.kv_compact_raw(**{**ok, f: None}) == -1, f
+    for kw in (dict(B=0), dict(B=4097), dict(N=0), dict(N=2**31), dict(kv_pool=FAKE + 8)):
+        assert pkg.kv_compact_raw(**{**ok, **kw}) == -2, kw
