@@ -265,6 +265,29 @@ def _event_mean_us(stream, fn, reps, warmup=3):
     return e0.elapsed_time(e1) * 1e3 / reps
 
 
+def _graph_mean_us(stream, fn, per_graph, replays=5):
+    """Mean device time of fn() with the host out of the loop: per_graph calls captured into one graph,
+    replayed `replays` times between HIP events on `stream`."""
+    import torch
+    with torch.cuda.stream(stream):
+        fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(per_graph):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(replays):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (replays * per_graph)
+
+
 def measure_tree_mask(inp, stream, dev, reps=50):
     """Device tree -> mask builder on the workload's trees: time per call, bytes written, parity."""
     import numpy as np
@@ -277,16 +300,18 @@ def measure_tree_mask(inp, stream, dev, reps=50):
     mask = torch.empty(total, dtype=torch.uint8, device=dev)
     indptr = torch.empty(inp.B + 1, dtype=torch.int32, device=dev)
     status = torch.empty(1, dtype=torch.int32, device=dev)
-    us = _event_mean_us(stream, lambda: pkg.build_tree_mask(parents, kv_indptr, mask, indptr, status, stream=stream),
-                        reps)
+    call = lambda: pkg.build_tree_mask(parents, kv_indptr, mask, indptr, status, stream=stream)  # noqa: E731
+    eager_us = _event_mean_us(stream, call, reps)
+    us = _graph_mean_us(stream, call, reps)
     exact = bool(np.array_equal(mask.cpu().numpy(), inp.custom_mask)
                  and np.array_equal(indptr.cpu().numpy(), inp.mask_indptr) and int(status.item()) == 0)
     nbytes = total + 4 * (inp.B + 1) + 4 * parents.numel() + 4 * (inp.B + 1)
     gbs = nbytes / (us * 1e-6) / 1e9
-    return {"us_per_call": us, "mask_bytes": total, "algorithmic_bytes": nbytes, "achieved_GBs": gbs,
+    return {"us_per_call": us, "timing": "graph of back-to-back calls, HIP events", "eager_us_per_call": eager_us,
+            "mask_bytes": total, "algorithmic_bytes": nbytes, "achieved_GBs": gbs,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS},
-            "launches_per_call": 2, "bit_exact_vs_generator": exact, "reps": reps}
+            "launches_per_call": 1, "bit_exact_vs_generator": exact, "reps": reps}
 
 
 def measure_kv_compact(inp, wl, stream, dev, partial_us_scattered, nsplit, reps=10):
@@ -314,6 +339,15 @@ def measure_kv_compact(inp, wl, stream, dev, partial_us_scattered, nsplit, reps=
                                                for b in range(inp.B)])))
     nbytes = 2 * tot * 1152 + 8 * tot
     gbs = nbytes / (us * 1e-6) / 1e9
+    # a plain contiguous device copy of the same byte count, as the practical ceiling of read + write
+    csrc = torch.empty(tot * 1152, dtype=torch.uint8, device=dev).fill_(1)
+    cdst = torch.empty_like(csrc)
+
+    def plain_copy():
+        with torch.cuda.stream(stream):
+            cdst.copy_(csrc)
+    copy_us = _event_mean_us(stream, plain_copy, reps, warmup=1)
+    del csrc, cdst
     # the partial kernel over the compacted prefix rows (draft rows stay where they are)
     ws = torch.empty(pkg.workspace_size(inp.B, inp.q_len, inp.H, nsplit), dtype=torch.uint8, device=dev)
     q_nope = torch.from_numpy(inp.q_nope.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -331,6 +365,7 @@ def measure_kv_compact(inp, wl, stream, dev, partial_us_scattered, nsplit, reps=
     return {"us_per_call": us, "rows_moved": tot, "algorithmic_bytes": nbytes, "achieved_GBs": gbs,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS},
+            "plain_copy_GBs": 2 * tot * 1152 / (copy_us * 1e-6) / 1e9, "vs_plain_copy": copy_us / us,
             "indices_exact": ok, "partial_us_scattered": partial_us_scattered, "partial_us_compacted": part_us,
             "break_even_steps": (us / (partial_us_scattered - part_us)) if partial_us_scattered > part_us else None,
             "reps": reps}

@@ -5,12 +5,13 @@
 //
 //   kv_compact_check_kernel  one workgroup: checks every destination run against the pool and
 //                            writes the status word.
-//   kv_compact_kernel        a fixed grid of waves over the concatenated prefix rows of all
-//                            requests (so ragged batches spread evenly). A wave moves 8 rows per
+//   kv_compact_kernel        one wave of resident workgroups striding over the concatenated prefix
+//                            rows of all requests (so ragged batches spread evenly). A wave moves 8 rows per
 //                            step: lanes 0-7 resolve one row each (request by binary search over
 //                            the running sum of prefix lengths held in LDS, source and destination
 //                            slot, new index), then every lane moves nine 16-byte pieces of those
-//                            8 x 1152 bytes, all nine loads issued before the first store.
+//                            8 x 1152 bytes, all nine loads issued before the first store. Loads and
+//                            stores are non-temporal: each byte is touched once.
 //
 // The work is one read and one write of each 1152-byte row: bound by HBM bandwidth.
 #include <hip/hip_runtime.h>
@@ -24,7 +25,7 @@ namespace {
 constexpr int kCheckThreads = 1024;
 constexpr int kCopyThreads = 256;
 constexpr int kCopyWaves = kCopyThreads / 64;
-constexpr int kCopyBlocks = 2048;           // fixed grid: 8192 waves, about 32 per CU
+constexpr int kCopyBlocksFallback = 2048;  // grid when the occupancy query fails
 constexpr int kRowBytes = MLA_VERIFY_ROW * 2;
 constexpr int kPiecesPerRow = kRowBytes / 16;  // 72 sixteen-byte pieces
 constexpr int kRowsPerStep = 8;
@@ -124,11 +125,13 @@ __global__ __launch_bounds__(kCopyThreads) void kv_compact_kernel(uint8_t* __res
       part_of[q] = p - r * kPiecesPerRow;
       const int s = __shfl(src, r, 64);
       dst_of[q] = __shfl(dst, r, 64);
-      piece[q] = reinterpret_cast<const u32x4*>(pool + (size_t)(s >= 0 ? s : 0) * kRowBytes)[part_of[q]];
+      piece[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pool + (size_t)(s >= 0 ? s : 0) * kRowBytes) +
+                                            part_of[q]);
     }
 #pragma unroll
     for (int q = 0; q < kPiecesPerLane; ++q)
-      if (dst_of[q] >= 0) reinterpret_cast<u32x4*>(pool + (size_t)dst_of[q] * kRowBytes)[part_of[q]] = piece[q];
+      if (dst_of[q] >= 0)
+        __builtin_nontemporal_store(piece[q], reinterpret_cast<u32x4*>(pool + (size_t)dst_of[q] * kRowBytes) + part_of[q]);
   }
 }
 
@@ -143,7 +146,18 @@ extern "C" int mla_verify_kv_compact(void* kv_pool, int64_t N, const int32_t* kv
   hipLaunchKernelGGL(kv_compact_check_kernel, dim3(1), dim3(kCheckThreads), 0, stream, kv_indptr, dst_start, B,
                      (long long)N, status);
   if (hipGetLastError() != hipSuccess) return MLA_VERIFY_ERR_LAUNCH;
-  hipLaunchKernelGGL(kv_compact_kernel, dim3(kCopyBlocks), dim3(kCopyThreads), (B + 1) * sizeof(long long), stream,
+  // One wave of resident workgroups (the grid-stride loop spreads the rows evenly); a larger grid
+  // leaves a partly filled last wave of workgroups that costs as much as a full one.
+  const size_t lds = (B + 1) * sizeof(long long);
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kv_compact_kernel, kCopyThreads, lds) != hipSuccess) {
+    (void)hipGetLastError();  // a failed query must not read as a failed launch below
+    cus = per_cu = 0;
+  }
+  const int grid = (cus > 0 && per_cu > 0) ? cus * per_cu : kCopyBlocksFallback;
+  hipLaunchKernelGGL(kv_compact_kernel, dim3(grid), dim3(kCopyThreads), lds, stream,
                      static_cast<uint8_t*>(kv_pool), (long long)N, kv_indptr, kv_indices, dst_start, B,
                      new_kv_indices, status);
   return hipGetLastError() == hipSuccess ? MLA_VERIFY_OK : MLA_VERIFY_ERR_LAUNCH;

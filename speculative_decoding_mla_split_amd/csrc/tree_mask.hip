@@ -1,11 +1,15 @@
 // Device-side builder of the tree visibility mask read by the verify attention (gfx950).
 //
 // The serving loop of "From Capture Safety to MoE Ceiling" (section "Phase 2e: The Occupancy
-// Epiphany and the 3-6x Speedup") built the mask on the host for every step. Here it is two
+// Epiphany and the 3-6x Speedup") built the mask on the host for every step. Here it is one or two
 // small kernels on the caller's stream, capturable with the attention:
 //
-//   tree_offsets_kernel  one workgroup: mask_indptr as the running sum of q_len * (P_b + q_len)
-//                        (64-bit, clamped to the capacity), the parent checks and the status word.
+//   tree_fused_kernel    small batches (B <= 1024, B * q_len <= 8192), one launch: each workgroup
+//                        sums the mask sizes before its request itself, then fills like
+//                        tree_fill_kernel; workgroup (0, 0) also writes the status word.
+//   tree_offsets_kernel  larger batches, one workgroup: mask_indptr as the running sum of
+//                        q_len * (P_b + q_len) (64-bit, clamped to the capacity), the parent
+//                        checks and the status word; then
 //   tree_fill_kernel     grid (X, B): request b's rows, 16 bytes per lane per step over aligned
 //                        16-byte chunks of the output. A chunk that lies inside one row's prefix
 //                        columns is a single 16-byte store of ones; other chunks compute each
@@ -25,7 +29,9 @@ namespace {
 
 constexpr int kOffsetThreads = 1024;
 constexpr int kFillThreads = 256;
-constexpr int kFillBlocksTarget = 4096;  // workgroups of one fill launch (spread over the requests)
+constexpr int kFillBlocksTarget = 1024;  // workgroups of one fill launch (spread over the requests)
+constexpr int kFusedMaxB = 1024;          // single-launch form up to this many requests ...
+constexpr int kFusedMaxParents = 8192;    // ... and this many parent entries (checked by one workgroup)
 
 __device__ __forceinline__ long long prefix_len(const int32_t* kv_indptr, int b) {
   const long long p = (long long)kv_indptr[b + 1] - (long long)kv_indptr[b];
@@ -82,16 +88,12 @@ __device__ __forceinline__ uint32_t ancestor_or_self(const int* par, int i, int 
   return k == j ? 1u : 0u;
 }
 
-__global__ __launch_bounds__(kFillThreads) void tree_fill_kernel(const int32_t* __restrict__ parents,
-                                                                 const int32_t* __restrict__ kv_indptr,
-                                                                 int q_len, uint8_t* __restrict__ custom_mask,
-                                                                 const int32_t* __restrict__ mask_indptr) {
-  __shared__ int par[MLA_TREE_MAX_QLEN];
-  const int b = blockIdx.y;
-  const long long P = prefix_len(kv_indptr, b);
+// Writes request b's q_len rows of P + q_len bytes at custom_mask[start, end); this workgroup
+// takes the 16-byte chunks blockIdx.x, blockIdx.x + gridDim.x, ... of them.
+__device__ __forceinline__ void fill_request(const int32_t* __restrict__ parents, int b, int q_len, long long P,
+                                             long long start, long long end, uint8_t* __restrict__ custom_mask,
+                                             int* par) {
   const long long L = P + q_len;
-  const long long start = mask_indptr[b], end = mask_indptr[b + 1];
-  if (end - start != (long long)q_len * L) return;  // did not fit the capacity: left unwritten
   for (int k = threadIdx.x; k < q_len; k += kFillThreads) {
     const int p = parents[(long long)b * q_len + k];
     par[k] = (p < -1 || p >= k) ? -1 : p;
@@ -133,6 +135,65 @@ __global__ __launch_bounds__(kFillThreads) void tree_fill_kernel(const int32_t* 
   }
 }
 
+__global__ __launch_bounds__(kFillThreads) void tree_fill_kernel(const int32_t* __restrict__ parents,
+                                                                 const int32_t* __restrict__ kv_indptr,
+                                                                 int q_len, uint8_t* __restrict__ custom_mask,
+                                                                 const int32_t* __restrict__ mask_indptr) {
+  __shared__ int par[MLA_TREE_MAX_QLEN];
+  const int b = blockIdx.y;
+  const long long P = prefix_len(kv_indptr, b);
+  const long long start = mask_indptr[b], end = mask_indptr[b + 1];
+  if (end - start != (long long)q_len * (P + q_len)) return;  // did not fit the capacity: left unwritten
+  fill_request(parents, b, q_len, P, start, end, custom_mask, par);
+}
+
+__device__ __forceinline__ long long block_sum(long long x, long long* red) {
+  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
+  __syncthreads();  // red may still be read by an earlier call
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  long long t = 0;
+  for (int w = 0; w < kFillThreads / 64; ++w) t += red[w];
+  return t;
+}
+
+// Single-launch form for small batches: every workgroup sums the mask sizes of the requests before
+// its own, workgroup (0, b) writes mask_indptr[b + 1], and workgroup (0, 0) also checks every parent
+// and the capacity and writes the status word.
+__global__ __launch_bounds__(kFillThreads) void tree_fused_kernel(const int32_t* __restrict__ parents,
+                                                                  const int32_t* __restrict__ kv_indptr, int B,
+                                                                  int q_len, long long limit,
+                                                                  uint8_t* __restrict__ custom_mask,
+                                                                  int32_t* __restrict__ mask_indptr,
+                                                                  int32_t* __restrict__ status) {
+  __shared__ int par[MLA_TREE_MAX_QLEN];
+  __shared__ long long red[kFillThreads / 64];
+  const int b = blockIdx.y;
+  long long part = 0;
+  for (int k = threadIdx.x; k < b; k += kFillThreads) part += (long long)q_len * (prefix_len(kv_indptr, k) + q_len);
+  const long long start = block_sum(part, red);
+  const long long P = prefix_len(kv_indptr, b);
+  const long long end = start + (long long)q_len * (P + q_len);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    mask_indptr[b + 1] = (int32_t)(end < limit ? end : limit);
+    if (b == 0) mask_indptr[0] = 0;
+  }
+  if (blockIdx.x == 0 && b == 0) {
+    long long tot = 0;
+    int bad = 0;
+    for (int k = threadIdx.x; k < B; k += kFillThreads) tot += (long long)q_len * (prefix_len(kv_indptr, k) + q_len);
+    for (int k = threadIdx.x; k < B * q_len; k += kFillThreads) {
+      const int p = parents[k];
+      bad |= (p < -1 || p >= k % q_len);
+    }
+    tot = block_sum(tot, red);
+    bad = __syncthreads_or(bad);
+    if (threadIdx.x == 0) *status = (bad ? MLA_TREE_BAD_PARENT : 0) | (tot > limit ? MLA_TREE_CAPACITY : 0);
+  }
+  if (end > limit) return;  // does not fit the capacity: left unwritten
+  fill_request(parents, b, q_len, P, start, end, custom_mask, par);
+}
+
 }  // namespace
 
 extern "C" int mla_verify_tree_mask(const int32_t* parents, const int32_t* kv_indptr, int B, int q_len,
@@ -142,10 +203,15 @@ extern "C" int mla_verify_tree_mask(const int32_t* parents, const int32_t* kv_in
   if (B < 1 || B > MLA_TREE_MAX_B || q_len < 1 || q_len > MLA_TREE_MAX_QLEN || mask_capacity < 0)
     return MLA_VERIFY_ERR_SHAPE;
   const long long limit = mask_capacity < INT32_MAX ? mask_capacity : INT32_MAX;
+  const int x = (kFillBlocksTarget + B - 1) / B;
+  if (B <= kFusedMaxB && (long long)B * q_len <= kFusedMaxParents) {
+    hipLaunchKernelGGL(tree_fused_kernel, dim3(x, B), dim3(kFillThreads), 0, stream, parents, kv_indptr, B, q_len,
+                       limit, custom_mask, mask_indptr, status);
+    return hipGetLastError() == hipSuccess ? MLA_VERIFY_OK : MLA_VERIFY_ERR_LAUNCH;
+  }
   hipLaunchKernelGGL(tree_offsets_kernel, dim3(1), dim3(kOffsetThreads), 0, stream, parents, kv_indptr, B, q_len,
                      limit, mask_indptr, status);
   if (hipGetLastError() != hipSuccess) return MLA_VERIFY_ERR_LAUNCH;
-  const int x = (kFillBlocksTarget + B - 1) / B;
   hipLaunchKernelGGL(tree_fill_kernel, dim3(x, B), dim3(kFillThreads), 0, stream, parents, kv_indptr, q_len,
                      custom_mask, mask_indptr);
   return hipGetLastError() == hipSuccess ? MLA_VERIFY_OK : MLA_VERIFY_ERR_LAUNCH;

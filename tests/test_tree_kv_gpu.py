@@ -85,6 +85,21 @@ def test_negative_prefix_length_and_large_tree():
     _check(_forest(rng, 3, 300, 0.02), np.array([50, 10, 60, 61]))
 
 
+@pytest.mark.parametrize("B,q_len", [(40, 256), (1100, 2)])
+def test_two_launch_path_for_large_batches(B, q_len):
+    """More than 8192 parent entries or more than 1024 requests: offsets kernel, then the fill."""
+    rng = np.random.default_rng(B)
+    prefixes = rng.integers(0, 60, B)
+    par = _forest(rng, B, q_len)
+    par[B // 2, q_len - 1] = q_len            # one bad parent
+    kv_indptr = np.concatenate([[0], np.cumsum(prefixes)])
+    _, _, st = _check(par, kv_indptr)
+    assert st == T.TREE_BAD_PARENT
+    ref, ip, _ = T.build_tree_mask(par.reshape(-1), kv_indptr, B, q_len)
+    _, got_ip, st = _check(par, kv_indptr, capacity=int(ip[B // 3]) + 7)
+    assert st == T.TREE_CAPACITY | T.TREE_BAD_PARENT
+
+
 def test_bad_parents_flagged():
     rng = np.random.default_rng(10)
     par = _forest(rng, 3, 12)
