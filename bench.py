@@ -3,9 +3,11 @@
 
 Prints ONE JSON line. A step is one verify call: the partial kernel plus the combine kernel over
 one batch of seeded synthetic inputs already resident in HBM. The default workload is the ragged
-B=4 batch with prefixes 4096/32768/120000/185000, q_len 16, H 64, nsplit 64, scattered slots in a
-2M-row pool. `value` is the effective KV bandwidth (sum of L_b * 1152 bytes per step / time per
-step); `ms_per_step` is the wall-clock time per step over the timed region.
+B=4 batch with prefixes 4096/32768/120000/185000, q_len 16, H 64, scattered slots in a 2M-row
+pool, under the balanced schedule with a budget of one workgroup per CU (units = CUs / 128-row
+tiles = 32 on MI355X); --schedule per-request --nsplit 64 runs nsplit splits per request instead.
+`value` is the effective KV bandwidth (sum of L_b * 1152 bytes per step / time per step);
+`ms_per_step` is the wall-clock time per step over the timed region.
 
 The roofline object covers the dominant kernel (the partial kernel): its algorithmic flops (or
 bytes, when the workload sits below the MFMA ridge) per launch over its average duration, timed
@@ -46,7 +48,7 @@ def algorithmic(inp):
 class Workload:
     """Device buffers of one configuration and the library calls on them."""
 
-    def __init__(self, wl, layout, nsplit, dev):
+    def __init__(self, wl, layout, nsplit, dev, balanced=False):
         import numpy as np
         import torch
 
@@ -54,7 +56,7 @@ class Workload:
         import workloads as W
 
         self.pkg, self.torch, self.np, self.W = pkg, torch, np, W
-        self.wl, self.layout, self.nsplit = wl, layout, nsplit
+        self.wl, self.layout, self.nsplit, self.balanced = wl, layout, nsplit, balanced
         self.inp = W.make_inputs(wl, layout=layout)
         inp = self.inp
         self.dev = dev
@@ -73,7 +75,9 @@ class Workload:
         self.kv_indptr, self.kv_indices = t(inp.kv_indptr), t(inp.kv_indices)
         self.out_cache_loc, self.custom_mask, self.mask_indptr = t(inp.out_cache_loc), t(inp.custom_mask), t(
             inp.mask_indptr)
-        self.ws_bytes = pkg.workspace_size(inp.B, inp.q_len, inp.H, nsplit)
+        size = pkg.balanced_workspace_size if balanced else pkg.workspace_size
+        self.ws_bytes = size(inp.B, inp.q_len, inp.H, nsplit)
+        assert self.ws_bytes > 0
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
         self.out = torch.empty((inp.B, inp.q_len, inp.H, 512), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((inp.B, inp.q_len, inp.H), dtype=torch.float32, device=dev)
@@ -81,16 +85,18 @@ class Workload:
 
     def partial(self, stream):
         inp = self.inp
-        rc = self.pkg.partial_raw(self.q_nope.data_ptr(), self.q_rope.data_ptr(), self.pool.data_ptr(), inp.N,
-                                  self.kv_indptr.data_ptr(), self.kv_indices.data_ptr(), self.out_cache_loc.data_ptr(),
-                                  self.custom_mask.data_ptr(), self.mask_indptr.data_ptr(), inp.B, inp.q_len, inp.H,
-                                  inp.scale, self.nsplit, self.ws.data_ptr(), self.ws_bytes, stream.cuda_stream)
+        call = self.pkg.balanced_partial_raw if self.balanced else self.pkg.partial_raw
+        rc = call(self.q_nope.data_ptr(), self.q_rope.data_ptr(), self.pool.data_ptr(), inp.N,
+                  self.kv_indptr.data_ptr(), self.kv_indices.data_ptr(), self.out_cache_loc.data_ptr(),
+                  self.custom_mask.data_ptr(), self.mask_indptr.data_ptr(), inp.B, inp.q_len, inp.H,
+                  inp.scale, self.nsplit, self.ws.data_ptr(), self.ws_bytes, stream.cuda_stream)
         assert rc == 0, self.pkg.status_string(rc)
 
     def combine(self, stream):
         inp = self.inp
-        rc = self.pkg.combine_raw(self.ws.data_ptr(), self.ws_bytes, inp.B, inp.q_len, inp.H, self.nsplit,
-                                  self.out.data_ptr(), self.lse.data_ptr(), stream.cuda_stream)
+        call = self.pkg.balanced_combine_raw if self.balanced else self.pkg.combine_raw
+        rc = call(self.ws.data_ptr(), self.ws_bytes, inp.B, inp.q_len, inp.H, self.nsplit,
+                  self.out.data_ptr(), self.lse.data_ptr(), stream.cuda_stream)
         assert rc == 0, self.pkg.status_string(rc)
 
     def step(self, stream):
@@ -223,11 +229,11 @@ def kernel_source_sha():
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
 
 
-def measured_traffic(workload, nsplit):
+def measured_traffic(workload, split_tag):
     """HBM bytes per partial-kernel launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary,
     scaled by the same counters' reading for a plain copy of known size; None when there is no
     summary for this workload or the kernel source changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_verify_partial_{workload}_ns{nsplit}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_verify_partial_{workload}_{split_tag}.json")
     if not os.path.exists(path):
         return None, "no counter summary"
     t = json.load(open(path))
@@ -314,7 +320,7 @@ def measure_tree_mask(inp, stream, dev, reps=50):
             "launches_per_call": 1, "bit_exact_vs_generator": exact, "reps": reps}
 
 
-def measure_kv_compact(inp, wl, stream, dev, partial_us_scattered, nsplit, reps=10):
+def measure_kv_compact(inp, wl, stream, dev, partial_us_scattered, nsplit, balanced, reps=10):
     """KV compaction of every prefix row into runs past the pool's used rows: time, bandwidth, and the
     partial kernel's time on the compacted indices next to the scattered ones."""
     import numpy as np
@@ -349,7 +355,8 @@ def measure_kv_compact(inp, wl, stream, dev, partial_us_scattered, nsplit, reps=
     copy_us = _event_mean_us(stream, plain_copy, reps, warmup=1)
     del csrc, cdst
     # the partial kernel over the compacted prefix rows (draft rows stay where they are)
-    ws = torch.empty(pkg.workspace_size(inp.B, inp.q_len, inp.H, nsplit), dtype=torch.uint8, device=dev)
+    size = pkg.balanced_workspace_size if balanced else pkg.workspace_size
+    ws = torch.empty(size(inp.B, inp.q_len, inp.H, nsplit), dtype=torch.uint8, device=dev)
     q_nope = torch.from_numpy(inp.q_nope.view(np.int16)).to(dev).view(torch.bfloat16)
     q_rope = torch.from_numpy(inp.q_rope.view(np.int16)).to(dev).view(torch.bfloat16)
     occ = torch.from_numpy(inp.out_cache_loc).to(dev)
@@ -357,7 +364,8 @@ def measure_kv_compact(inp, wl, stream, dev, partial_us_scattered, nsplit, reps=
     mip = torch.from_numpy(inp.mask_indptr).to(dev)
 
     def part():
-        rc = pkg.partial_raw(q_nope.data_ptr(), q_rope.data_ptr(), pool.data_ptr(), N, kv_indptr.data_ptr(),
+        call = pkg.balanced_partial_raw if balanced else pkg.partial_raw
+        rc = call(q_nope.data_ptr(), q_rope.data_ptr(), pool.data_ptr(), N, kv_indptr.data_ptr(),
                              new_idx.data_ptr(), occ.data_ptr(), cmask.data_ptr(), mip.data_ptr(), inp.B, inp.q_len,
                              inp.H, inp.scale, nsplit, ws.data_ptr(), ws.numel(), stream.cuda_stream)
         assert rc == 0
@@ -382,7 +390,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="ragged4_185k_h64")
     ap.add_argument("--layout", default=None)
-    ap.add_argument("--nsplit", type=int, default=None)
+    ap.add_argument("--nsplit", type=int, default=None,
+                    help="per-request schedule: splits per request (default: the workload's largest)")
+    ap.add_argument("--schedule", choices=("balanced", "per-request"), default="balanced",
+                    help="balanced: one split budget for the batch (mla_verify_attn_balanced); "
+                         "per-request: nsplit splits per request (mla_verify_attn)")
+    ap.add_argument("--units", type=int, default=None,
+                    help="balanced schedule: split budget (default: CUs / 128-row tiles, one workgroup per CU)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true", help="skip the 16k/65k configuration sweep")
@@ -410,10 +424,15 @@ def main():
     dev = torch.device("cuda:0")
     wl = W.CONFIGS[args.config]
     layout = args.layout or wl.layout
-    nsplit = args.nsplit or wl.nsplits[-1]
+    balanced = args.schedule == "balanced"
+    n_rt = -(-wl.q_len * wl.H // 128)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    units = args.units or max(wl.B, cus // n_rt)
+    nsplit = units if balanced else (args.nsplit or wl.nsplits[-1])
     stream = torch.cuda.Stream(device=dev)
-    print(f"[bench] {wl.name} layout={layout} nsplit={nsplit}", file=sys.stderr, flush=True)
-    wk = Workload(wl, layout, nsplit, dev)
+    print(f"[bench] {wl.name} layout={layout} schedule={args.schedule} "
+          f"{'units' if balanced else 'nsplit'}={nsplit}", file=sys.stderr, flush=True)
+    wk = Workload(wl, layout, nsplit, dev, balanced=balanced)
     wall, part, comb, stepu = wk.time_steps(stream, args.steps, args.warmup)
     print(f"[bench] timed {args.steps} steps: {wall:.1f} us/step", file=sys.stderr, flush=True)
     parity = wk.parity(args.parity_rows)
@@ -423,7 +442,7 @@ def main():
     value = alg["kv_bytes"] / (wall * 1e-6) / 1e9
     floor = step_floor_us(alg)
     roof = roofline_for(wk, part_s["mean"])
-    traffic, traffic_src = measured_traffic(wl.name, nsplit)
+    traffic, traffic_src = measured_traffic(wl.name, ("u" if balanced else "ns") + str(nsplit))
     roof["traffic"] = traffic
     roof["traffic_source"] = traffic_src
     result = {
@@ -431,7 +450,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": wall / 1e3, "us_per_step": wall, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "prefixes": list(wl.prefixes), "q_len": wl.q_len, "H": wl.H,
-                   "pool_rows": wl.N, "layout": layout, "nsplit": nsplit, "seed": wl.seed,
+                   "pool_rows": wl.N, "layout": layout, "schedule": args.schedule,
+                   ("units" if balanced else "nsplit"): nsplit, "seed": wl.seed,
                    "scale": "1/sqrt(192)", "parallelism": "single GPU"},
         "roofline": roof,
         "kernels_us": {"partial": part_s, "combine": comb_s, "step_events": stats(stepu)},
@@ -448,12 +468,24 @@ def main():
         print("[bench] tree mask builder", file=sys.stderr, flush=True)
         nxt = {"tree_mask": measure_tree_mask(main_inp, stream, dev)}
         print("[bench] kv compaction", file=sys.stderr, flush=True)
-        nxt["kv_compact"] = measure_kv_compact(main_inp, wl, stream, dev, part_s["mean"], nsplit)
+        nxt["kv_compact"] = measure_kv_compact(main_inp, wl, stream, dev, part_s["mean"], nsplit, balanced)
         result["next_rows"] = nxt
         torch.cuda.empty_cache()
 
     if not args.no_others:
         others = []
+        # the ragged batch under both schedules (hot, back-to-back steps)
+        for sched, ns in (("per-request", 32), ("per-request", 64), ("per-request", 128),
+                          ("balanced", 32), ("balanced", 64), ("balanced", 128)):
+            print(f"[bench] sweep {wl.name} {sched} {ns}", file=sys.stderr, flush=True)
+            ow = Workload(wl, layout, ns, dev, balanced=sched == "balanced")
+            hot_wall, hp, hc, hs = ow.time_steps(stream, 20, 3)
+            others.append({"workload": wl.name, "layout": layout, "schedule": sched,
+                           ("units" if sched == "balanced" else "nsplit"): ns, "hot_us_per_step": hot_wall,
+                           "partial_us_hot": stats(hp)["mean"], "combine_us_hot": stats(hc)["mean"],
+                           "partial_roofline": roofline_for(ow, stats(hp)["mean"])})
+            del ow
+            torch.cuda.empty_cache()
         scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         for name, lay, ns in (("16k_h64", "contiguous", 16), ("16k_h64", "scattered", 16),
                               ("16k_h64", "scattered", 32), ("16k_h64", "scattered", 64),
@@ -465,7 +497,7 @@ def main():
             a = ow.alg
             fl = step_floor_us(a)
             others.append({
-                "workload": name, "layout": lay, "nsplit": ns,
+                "workload": name, "layout": lay, "schedule": "per-request", "nsplit": ns,
                 "hot_us_per_step": hot_wall, "hot_kv_GBs": a["kv_bytes"] / (hot_wall * 1e-6) / 1e9,
                 "cold_step_us_median": stats(cs)["median"],
                 "cold_kv_GBs": a["kv_bytes"] / (stats(cs)["median"] * 1e-6) / 1e9,

@@ -58,6 +58,8 @@ typedef enum {
 #define MLA_VERIFY_ROW 576             /* bf16 values per KV pool row (1152 bytes) */
 #define MLA_VERIFY_MAX_NSPLIT 1024
 #define MLA_VERIFY_WORKSPACE_ALIGN 256 /* required alignment of the workspace pointer */
+#define MLA_VERIFY_MAX_UNITS 4096      /* largest `units` of the balanced entry points */
+#define MLA_VERIFY_BALANCED_MAX_B 4096 /* largest B of the balanced entry points */
 
 /*
  * Bytes of workspace mla_verify_attn needs for these sizes ("From Capture Safety to MoE
@@ -140,6 +142,54 @@ int mla_verify_attn_partial(const void *q_nope, const void *q_rope, const void *
 
 int mla_verify_attn_combine(const void *workspace, size_t workspace_bytes, int B, int q_len, int H,
                             int nsplit, void *out, float *lse, hipStream_t stream);
+
+/*
+ * Balanced partition of the same computation. The per-request splits above give every request
+ * nsplit splits whatever its length, so in a ragged batch the short requests' workgroups finish
+ * early while the long ones' run on, and every split writes a partial. Here `units` is a split
+ * budget for the whole batch (B <= units <= MLA_VERIFY_MAX_UNITS). Request b has T_b =
+ * ceil(L_b / 32) column tiles; the device takes the smallest split size C (in tiles) with
+ * sum_b ceil(T_b / C) <= units, gives request b n_b = ceil(T_b / C) splits and cuts its tiles
+ * evenly: split s covers tiles [floor(s T_b / n_b), floor((s+1) T_b / n_b)) (columns clipped to
+ * L_b). The largest split is as small as any such partition allows, so a fixed grid of
+ * units * ceil(q_len * H / 128) workgroups is filled with near-equal work; budget left over by the
+ * rounding exits at once. Sources: "From Capture Safety to MoE Ceiling", section "The Architecture
+ * of Capture Safety" (a fixed grid with chunk bounds computed on the device from the actual lengths)
+ * and section "The Occupancy Calculation" (the split count is chosen to fill every SM); "The Custom
+ * sm_120 Verify Kernel", section "Building the Custom Kernel" (per-split partials and a second
+ * reduction kernel).
+ *
+ * Arguments and rules are those of mla_verify_attn, with `units` in place of nsplit (the launch
+ * shape depends on (B, q_len, H, units) only; a multiple of 8 keeps the XCDs equally loaded) and
+ * B <= MLA_VERIFY_BALANCED_MAX_B. units outside [B, MLA_VERIFY_MAX_UNITS] returns
+ * MLA_VERIFY_ERR_NSPLIT. The result equals mla_verify_attn's up to rounding order; with units = B
+ * every request gets one split and the result is bit-identical to mla_verify_attn with nsplit = 1.
+ *
+ * The workspace holds the plan (split_start int32 [B + 1]: the running sum of n_b; req_of_split
+ * int32 [units]: the request of each split, -1 if unused), then float2 ml [units][q_len*H] and float
+ * acc [units][q_len*H][512] partials (split split_start[b] + s of request b at block
+ * split_start[b] + s), each region 256-byte aligned. mla_verify_attn_balanced_partial writes the plan
+ * (one-workgroup kernel) and the partials; mla_verify_attn_balanced_combine reads both.
+ * mla_verify_attn_balanced_workspace_size returns 0 for arguments out of range.
+ */
+size_t mla_verify_attn_balanced_workspace_size(int B, int q_len, int H, int units);
+
+int mla_verify_attn_balanced(const void *q_nope, const void *q_rope, const void *kv_pool, int64_t N,
+                             const int32_t *kv_indptr, const int32_t *kv_indices,
+                             const int32_t *out_cache_loc, const uint8_t *custom_mask,
+                             const int32_t *mask_indptr, int B, int q_len, int H, float scale, int units,
+                             void *workspace, size_t workspace_bytes, void *out, float *lse,
+                             hipStream_t stream);
+
+int mla_verify_attn_balanced_partial(const void *q_nope, const void *q_rope, const void *kv_pool,
+                                     int64_t N, const int32_t *kv_indptr, const int32_t *kv_indices,
+                                     const int32_t *out_cache_loc, const uint8_t *custom_mask,
+                                     const int32_t *mask_indptr, int B, int q_len, int H, float scale,
+                                     int units, void *workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
+int mla_verify_attn_balanced_combine(const void *workspace, size_t workspace_bytes, int B, int q_len,
+                                     int H, int units, void *out, float *lse, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -47,6 +47,14 @@ def library() -> ctypes.CDLL:
         lib.mla_verify_attn_partial.restype = i32
         lib.mla_verify_attn_combine.argtypes = [vp, sz, i32, i32, i32, i32, vp, vp, vp]
         lib.mla_verify_attn_combine.restype = i32
+        lib.mla_verify_attn_balanced_workspace_size.argtypes = [i32, i32, i32, i32]
+        lib.mla_verify_attn_balanced_workspace_size.restype = sz
+        lib.mla_verify_attn_balanced.argtypes = lib.mla_verify_attn.argtypes
+        lib.mla_verify_attn_balanced.restype = i32
+        lib.mla_verify_attn_balanced_partial.argtypes = lib.mla_verify_attn_partial.argtypes
+        lib.mla_verify_attn_balanced_partial.restype = i32
+        lib.mla_verify_attn_balanced_combine.argtypes = lib.mla_verify_attn_combine.argtypes
+        lib.mla_verify_attn_balanced_combine.restype = i32
         lib.mla_verify_tree_mask.argtypes = [vp, vp, i32, i32, vp, i64, vp, vp, vp]
         lib.mla_verify_tree_mask.restype = i32
         lib.mla_verify_kv_compact.argtypes = [vp, i64, vp, vp, vp, i32, vp, vp, vp]
@@ -86,6 +94,35 @@ def combine_raw(workspace, workspace_bytes, B, q_len, H, nsplit, out, lse, strea
                                                  int(nsplit), out, lse, stream))
 
 
+def balanced_workspace_size(B: int, q_len: int, H: int, units: int) -> int:
+    """Bytes of workspace verify_attn_balanced needs (0 if an argument is out of range)."""
+    return int(library().mla_verify_attn_balanced_workspace_size(int(B), int(q_len), int(H), int(units)))
+
+
+def balanced_raw(q_nope, q_rope, kv_pool, N, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
+                 B, q_len, H, scale, units, workspace, workspace_bytes, out, lse, stream) -> int:
+    """Direct call of mla_verify_attn_balanced with integer device addresses; returns the status."""
+    return int(library().mla_verify_attn_balanced(q_nope, q_rope, kv_pool, int(N), kv_indptr, kv_indices,
+                                                  out_cache_loc, custom_mask, mask_indptr, int(B), int(q_len),
+                                                  int(H), float(scale), int(units), workspace,
+                                                  int(workspace_bytes), out, lse, stream))
+
+
+def balanced_partial_raw(q_nope, q_rope, kv_pool, N, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
+                         B, q_len, H, scale, units, workspace, workspace_bytes, stream) -> int:
+    """Direct call of mla_verify_attn_balanced_partial; returns the status."""
+    return int(library().mla_verify_attn_balanced_partial(q_nope, q_rope, kv_pool, int(N), kv_indptr, kv_indices,
+                                                          out_cache_loc, custom_mask, mask_indptr, int(B),
+                                                          int(q_len), int(H), float(scale), int(units), workspace,
+                                                          int(workspace_bytes), stream))
+
+
+def balanced_combine_raw(workspace, workspace_bytes, B, q_len, H, units, out, lse, stream) -> int:
+    """Direct call of mla_verify_attn_balanced_combine; returns the status."""
+    return int(library().mla_verify_attn_balanced_combine(workspace, int(workspace_bytes), int(B), int(q_len),
+                                                          int(H), int(units), out, lse, stream))
+
+
 def tree_mask_raw(parents, kv_indptr, B, q_len, custom_mask, mask_capacity, mask_indptr, status, stream) -> int:
     """Direct call of mla_verify_tree_mask with integer device addresses; returns the status."""
     return int(library().mla_verify_tree_mask(parents, kv_indptr, int(B), int(q_len), custom_mask,
@@ -108,13 +145,15 @@ def _need(cond, msg):
 
 
 def verify_attn(q_nope, q_rope, kv_pool, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
-                scale: float, nsplit: int, workspace, out, lse, stream=None) -> None:
+                scale: float, nsplit: int, workspace, out, lse, stream=None, balanced: bool = False) -> None:
     """Tree-verify attention on torch device tensors (no copies, no host synchronisation).
 
     q_nope bf16 [B,q_len,H,512], q_rope bf16 [B,q_len,H,64], kv_pool bf16 [N,576],
     kv_indptr int32 [B+1], kv_indices int32, out_cache_loc int32 [B*q_len], custom_mask uint8/bool,
     mask_indptr int32 [>=B], workspace uint8 [>= workspace_size(...)], out bf16 [B,q_len,H,512],
     lse float32 [B,q_len,H]. stream: a torch.cuda.Stream (default: the current stream).
+    balanced=True runs mla_verify_attn_balanced with nsplit as the batch's split budget (`units`,
+    workspace from balanced_workspace_size).
     """
     import torch
 
@@ -136,7 +175,8 @@ def verify_attn(q_nope, q_rope, kv_pool, kv_indptr, kv_indices, out_cache_loc, c
           "index array lengths")
     if stream is None:
         stream = torch.cuda.current_stream(q_nope.device)
-    rc = attn_raw(q_nope.data_ptr(), q_rope.data_ptr(), kv_pool.data_ptr(), kv_pool.shape[0],
+    call = balanced_raw if balanced else attn_raw
+    rc = call(q_nope.data_ptr(), q_rope.data_ptr(), kv_pool.data_ptr(), kv_pool.shape[0],
                   kv_indptr.data_ptr(), kv_indices.data_ptr() if kv_indices.numel() else None,
                   out_cache_loc.data_ptr(), custom_mask.data_ptr(), mask_indptr.data_ptr(), B, q_len, H, scale,
                   nsplit, workspace.data_ptr(), workspace.numel(), out.data_ptr(), lse.data_ptr(),

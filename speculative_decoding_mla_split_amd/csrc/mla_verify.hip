@@ -72,6 +72,8 @@ static_assert(kLdsBytes + 64 <= 160 * 1024, "LDS budget of one CU");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -165,7 +167,6 @@ struct Ctx {
   int tok_first, tok_last, my_pair, my_half, n_tok_pairs;
   int n_meta;  // metadata loads per tile of this wave: 1 + extra mask loads (wave-uniform)
   float scale_log2;
-  int k_off[4], v_off0, v_off1;
 };
 
 // Metadata loads of one tile into a wave's ring stage m (x.n_meta instructions; PART > 0 is a no-op
@@ -295,7 +296,8 @@ struct Bufs {
 // never the ones read here, which lets the compiler drop its own blanket wait on those loads.
 __device__ __forceinline__ void tile_step(const Ctx& x, int t, int c_begin, const Glob& gl, const Bufs& bf,
                                           const bf16x8 (&q)[2][kHalfSteps], f32x16 (&oacc)[2][kHalfEBlocks],
-                                          float& m_ref, float& m_seen, float& l_lane, bool& over) {
+                                          float& m_ref, float& l_lane, bool& over,
+                                          float& best_raw, int& best_col) {
   const int tile_c0 = c_begin + t * kTile;
   // The metadata, mask and gather addresses derive from the lane's role; hiding those inputs behind
   // an empty asm makes the compiler rebuild the addresses in each step as short-lived values instead
@@ -303,6 +305,22 @@ __device__ __forceinline__ void tile_step(const Ctx& x, int t, int c_begin, cons
   Ctx xm = x;
   asm volatile("" : "+v"(xm.lane), "+v"(xm.g), "+v"(xm.my_pair), "+v"(xm.my_half));
   const uint8_t* __restrict__ kb = bf.kv + (t % kBufs) * kTileBytes;
+  // LDS offsets of this lane's K and V fragments, rebuilt each step from the opaque lane (cheaper
+  // than keeping six more registers live across the loop). K: the lane reads logical chunk
+  // 36hf + 2ks + g of tile row (lane & 31). V (transposed reads): the 16-lane group G reads tile rows
+  // 16kk + 8m + 4(G/2) + (k16/4), m = 0, 1, latent columns 32eb + 16(G%2) + 4(k16%4) .. +3 of block
+  // eb = 8hf + leb, i.e. logical chunk 4eb + vc with vc = 2(G%2) + (k16%4)/2; the hf part is folded
+  // into the offsets.
+  int k_off[4], v_off0, v_off1;
+#pragma unroll
+  for (int b4 = 0; b4 < 4; ++b4) k_off[b4] = tile_offset(xm.lane & 31, 36 * x.hf + 2 * b4 + xm.g);
+  {
+    const int k16 = xm.lane & 15, G = xm.lane >> 4;
+    const int v_row = 4 * (G >> 1) + (k16 >> 2);
+    const int v_chunk = 2 * (G & 1) + ((k16 & 3) >> 1);
+    v_off0 = tile_offset(v_row, 32 * x.hf + v_chunk) + (k16 & 1) * 8;
+    v_off1 = tile_offset(v_row, 32 * x.hf + 4 + v_chunk) + (k16 & 1) * 8;
+  }
   const KvGather gat = kv_gather_setup(xm, gl.kv_pool, bf.meta + ((t + 2) % kMetaStages) * kMetaBytes,
                                        bf.kv + ((t + 2) % kBufs) * kTileBytes);
   uint8_t* const meta_dst = bf.meta + ((t + 4) % kMetaStages) * kMetaBytes;
@@ -335,7 +353,7 @@ __device__ __forceinline__ void tile_step(const Ctx& x, int t, int c_begin, cons
     constexpr int kKAhead = 2;
     bf16x8 kf[kKAhead + 1];
     auto load_k = [&](int ks) {
-      kf[ks % (kKAhead + 1)] = *reinterpret_cast<const bf16x8*>(kb + x.k_off[ks % 4] + kGroupBytes * (ks / 4));
+      kf[ks % (kKAhead + 1)] = *reinterpret_cast<const bf16x8*>(kb + k_off[ks % 4] + kGroupBytes * (ks / 4));
     };
 #pragma unroll
     for (int ks = 0; ks < kKAhead; ++ks) load_k(ks);
@@ -371,8 +389,13 @@ __device__ __forceinline__ void tile_step(const Ctx& x, int t, int c_begin, cons
   // 3. mask + softmax numerators against the row's reference max m_ref (base-2 units of the scaled
   // score). The reference is the max of the first tile with a visible column and then stays fixed,
   // so the accumulators are never rescaled; a later score above m_ref + kHeadroom raises `over`,
-  // and the kernel then reruns the split with m_ref = the true max m_seen. Element i of s_own is
+  // and the kernel then reruns the split with m_ref = the row's true max. Element i of s_own is
   // column 8(i/4) + 4g + i%4 of the tile; bit c of `bits` marks column c visible for this lane's row.
+  // The low 4 mantissa bits of each score are replaced by its element index (a change of at most
+  // 15 ulp, far below the bf16 rounding of the probabilities), so the max below also names its
+  // element and every score is distinct within the lane.
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s_own[i] = __uint_as_float((__float_as_uint(s_own[i]) & ~15u) | (uint32_t)i);
   float raw = -INFINITY;  // max of the visible raw dot products (scale > 0)
   if (__all(bits == 0xFFFFFFFFu)) {  // every column visible for every row (prefix tiles)
 #pragma unroll
@@ -385,8 +408,15 @@ __device__ __forceinline__ void tile_step(const Ctx& x, int t, int c_begin, cons
       raw = fmaxf(raw, s_own[i]);
     }
   }
+  // the lane's largest visible score so far and its column (the index rides in the score's low
+  // bits; an earlier tile keeps a tie): the row's largest probability is put back at its exact
+  // value when the split ends
+  {
+    const int col = (int)(__float_as_uint(raw) & 15u);
+    best_col = raw > best_raw ? tile_c0 + 8 * (col >> 2) + 4 * x.g + (col & 3) : best_col;
+    best_raw = fmaxf(best_raw, raw);
+  }
   const float mx = pair_max(raw) * x.scale_log2;
-  m_seen = fmaxf(m_seen, mx);
   m_ref = m_ref == -INFINITY ? mx : m_ref;
   over = over || mx > m_ref + kHeadroom;
   const float base = m_ref == -INFINITY ? 0.0f : m_ref;
@@ -394,11 +424,14 @@ __device__ __forceinline__ void tile_step(const Ctx& x, int t, int c_begin, cons
   bf16x8 pb_own[2];
   float psum = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_own[i], x.scale_log2, -base));  // 2^-inf = 0
-    psum += p;
-    pb_own[i >> 3][i & 7] = (__bf16)p;
-    if (i == 7) {
+  for (int i = 0; i < 16; i += 2) {
+    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_own[i], x.scale_log2, -base));  // 2^-inf = 0
+    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_own[i + 1], x.scale_log2, -base));
+    const bf16x2 pk = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
+    psum += p0 + p1;
+    pb_own[i >> 3][i & 7] = pk[0];
+    pb_own[i >> 3][(i & 7) + 1] = pk[1];
+    if (i == 6) {
       __builtin_amdgcn_sched_barrier(0);
       loads(38);
       __builtin_amdgcn_sched_barrier(0);
@@ -423,7 +456,7 @@ __device__ __forceinline__ void tile_step(const Ctx& x, int t, int c_begin, cons
   auto load_v = [&](int f) {
     const int kk = f >> 3, leb = f & 7;  // leb: block of 32 output columns inside this wave's half
     // rows 16kk + 8m + v_row (regions 2kk + m), latent chunk 4(8hf + leb) + v_chunk
-    const uint8_t* p0 = kb + (leb & 1 ? x.v_off1 : x.v_off0) + 2 * kk * kRegionBytes + kGroupBytes * (leb >> 1);
+    const uint8_t* p0 = kb + (leb & 1 ? v_off1 : v_off0) + 2 * kk * kRegionBytes + kGroupBytes * (leb >> 1);
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + kRegionBytes));
     vf[f % (kVAhead + 1)] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -455,45 +488,59 @@ __device__ __forceinline__ void tile_step(const Ctx& x, int t, int c_begin, cons
 // metadata loads of tile t+4. Loads retire in order, so "at most 9 + n_meta outstanding" at the top
 // of step t means everything issued up to step t-2 (tile t's rows, tile t+2's metadata) has landed.
 // Prefetches past the split read clamped, valid addresses into buffers that are never read.
-__global__ void __launch_bounds__(kWaves * 64, 1)
-verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restrict__ q_rope,
-                      const uint8_t* __restrict__ kv_pool, int N,
-                      const int32_t* __restrict__ kv_indptr, const int32_t* __restrict__ kv_indices,
-                      const int32_t* __restrict__ out_cache_loc,
-                      const uint8_t* __restrict__ custom_mask,
-                      const int32_t* __restrict__ mask_indptr, int B, int q_len, int H,
-                      float scale_log2, int nsplit, int n_rt, float2* __restrict__ ws_ml,
-                      float* __restrict__ ws_acc) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_kv[kBufs * kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_s[kWaves * kSXchgBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_p[kWaves * kPXchgBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_meta[kWaves * kMetaStages * kMetaBytes];
+// Inputs of the partial kernels that every split reads.
+struct PartialArgs {
+  const __bf16* q_nope;
+  const __bf16* q_rope;
+  const uint8_t* kv_pool;
+  int N;
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  const int32_t* out_cache_loc;
+  const uint8_t* custom_mask;
+  const int32_t* mask_indptr;
+  int B, q_len, H;
+  float scale_log2;
+  float2* ws_ml;
+  float* ws_acc;
+};
 
+// The partial kernels' LDS.
+struct PartialLds {
+  uint8_t* kv;
+  uint8_t* s;
+  uint8_t* p;
+  uint8_t* meta;
+  int* over;
+};
+
+// Columns [c_begin, c_end) (c_begin < c_end) of request b for the 128 query rows of row tile rt:
+// writes the (m, l) and accumulator partials of those rows at partial row offset `part`.
+__device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds& lds, int b, int c_begin,
+                                          int c_end, int rt, size_t part) {
+  const __bf16* __restrict__ q_nope = a.q_nope;
+  const __bf16* __restrict__ q_rope = a.q_rope;
+  const uint8_t* __restrict__ kv_pool = a.kv_pool;
+  const int32_t* __restrict__ kv_indices = a.kv_indices;
+  const int32_t* __restrict__ out_cache_loc = a.out_cache_loc;
+  const uint8_t* __restrict__ custom_mask = a.custom_mask;
+  float2* __restrict__ ws_ml = a.ws_ml;
+  float* __restrict__ ws_acc = a.ws_acc;
+  const int H = a.H, q_len = a.q_len;
   const int lane = threadIdx.x & 63;
   const int w = wave_uniform(threadIdx.x >> 6);
   const int pr_id = w >> 1, hf = w & 1;
-  const Split sp = decode_unit(B, nsplit, n_rt);
-  if (!sp.valid) return;
-  const int b = sp.b, s = sp.s;
   const int R = q_len * H;
-
-  // ---- split bounds from the actual lengths (empty splits leave at once)
-  const int kv_start = kv_indptr[b];
-  const int P = max(kv_indptr[b + 1] - kv_start, 0);
+  const int kv_start = a.kv_indptr[b];
+  const int P = max(a.kv_indptr[b + 1] - kv_start, 0);
   const int L = P + q_len;
-  int chunk = (L + nsplit - 1) / nsplit;
-  chunk = (chunk + kTile - 1) / kTile * kTile;
-  const int c_begin = s * chunk;
-  const int c_end = min(L, c_begin + chunk);
 
   const int g = lane >> 5;  // k-group of the MFMA operands
-  const int pair_row0 = sp.rt * kRowsPerWG + pr_id * kRowsPerPair;
+  const int pair_row0 = rt * kRowsPerWG + pr_id * kRowsPerPair;
   // register set i of this wave holds row block i ^ hf of the pair: set 0 is the own block
   auto set_row = [&](int i) { return pair_row0 + kBlockRows * (i ^ hf) + (lane & 31); };
   const int own_row0 = pair_row0 + kBlockRows * hf;
   const int own_row = set_row(0);
-  const size_t part = ((size_t)b * nsplit + s) * R;
-
   if (c_begin >= c_end) {
     if (own_row < R && g == 0) ws_ml[part + own_row] = make_float2(-INFINITY, 0.0f);
     return;
@@ -517,8 +564,8 @@ verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restric
   }
 
   Ctx x;
-  x.mask_base = (size_t)mask_indptr[b];
-  x.N = N;
+  x.mask_base = (size_t)a.mask_indptr[b];
+  x.N = a.N;
   x.b = b;
   x.q_len = q_len;
   x.kv_start = kv_start;
@@ -538,32 +585,22 @@ verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restric
   x.n_tok_pairs = (x.tok_last - x.tok_first + 2) >> 1;
   // metadata loads per tile: the first carries token 0, each extra one two more tokens
   x.n_meta = 1 + min((x.tok_last - x.tok_first + 1) / 2, kMetaExtra);
-  x.scale_log2 = scale_log2;
-  // K-operand reads: lane reads logical chunk 36hf + 2ks + g of tile row (lane & 31)
-#pragma unroll
-  for (int b4 = 0; b4 < 4; ++b4) x.k_off[b4] = tile_offset(lane & 31, 36 * hf + 2 * b4 + g);
-  // transposed V reads: the 16-lane group G reads tile rows 16kk + 8m + 4(G/2) + (k16/4), m = 0, 1,
-  // latent columns 32eb + 16(G%2) + 4(k16%4) .. +3 of block eb = 8hf + leb, i.e. logical chunk
-  // 4eb + vc with vc = 2(G%2) + (k16%4)/2; the hf part (groups 4hf..) is folded into the offsets.
-  {
-    const int k16 = lane & 15, G = lane >> 4;
-    const int v_row = 4 * (G >> 1) + (k16 >> 2);
-    const int v_chunk = 2 * (G & 1) + ((k16 & 3) >> 1);
-    x.v_off0 = tile_offset(v_row, 32 * hf + v_chunk) + (k16 & 1) * 8;
-    x.v_off1 = tile_offset(v_row, 32 * hf + 4 + v_chunk) + (k16 & 1) * 8;
-  }
-  uint8_t* const meta = lds_meta + w * kMetaStages * kMetaBytes;
+  x.scale_log2 = a.scale_log2;
+  uint8_t* const meta = lds.meta + w * kMetaStages * kMetaBytes;
+  uint8_t* const lds_kv = lds.kv;
   const Bufs bf = {lds_kv, meta,
-                   lds_s + w * kSXchgBytes + lane * 16, lds_s + (w ^ 1) * kSXchgBytes + lane * 16,
-                   lds_p + w * kPXchgBytes + lane * 16, lds_p + (w ^ 1) * kPXchgBytes + lane * 16};
+                   lds.s + w * kSXchgBytes + lane * 16, lds.s + (w ^ 1) * kSXchgBytes + lane * 16,
+                   lds.p + w * kPXchgBytes + lane * 16, lds.p + (w ^ 1) * kPXchgBytes + lane * 16};
   const Glob gl = {kv_pool, kv_indices, out_cache_loc, custom_mask};
 
   const int ntiles = (c_end - c_begin + kTile - 1) / kTile;
   f32x16 oacc[2][kHalfEBlocks];
   float m_ref = -INFINITY;   // reference max of the own row (base-2 units), fixed once set
-  float m_seen = -INFINITY;  // true max of the own row over the split
   float l_lane = 0.0f;
-  __shared__ int lds_over[kWaves];
+  // the lane's largest visible raw score of the split (index bits included) and its column
+  float best_raw = -INFINITY;
+  int best_col = 0;
+  int* const lds_over = lds.over;
 
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
@@ -571,6 +608,8 @@ verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restric
 #pragma unroll
       for (int eb = 0; eb < kHalfEBlocks; ++eb) oacc[i][eb] = f32x16{};
     l_lane = 0.0f;
+    best_raw = -INFINITY;
+    best_col = 0;
     bool over = false;
 
     // ---- prologue, laid out like the steady state: ... rows(t+1), meta(t+3), rows(t+2), meta(t+4) ...
@@ -596,7 +635,7 @@ verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restric
       else
         __builtin_amdgcn_s_waitcnt((kLoadsPerWave + 3) | (0x7 << 4) | (0xF << 8));
       lds_barrier();  // tile t is in LDS; buffer (t+2)%3 and the exchange slots are free again
-      tile_step(x, t, c_begin, gl, bf, q, oacc, m_ref, m_seen, l_lane, over);
+      tile_step(x, t, c_begin, gl, bf, q, oacc, m_ref, l_lane, over, best_raw, best_col);
     }
     // the last iterations prefetched rows past the split; let them land before LDS is reused
     __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0)
@@ -610,7 +649,60 @@ verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restric
     for (int k = 0; k < kWaves; ++k) any_over |= lds_over[k];
     lds_barrier();
     if (!any_over) break;
-    m_ref = m_seen;
+    m_ref = pair_max(best_raw) * x.scale_log2;  // the row's true max over the split
+  }
+
+  // ---- exact top probability. Each visible column entered the PV product with its probability
+  // rounded to bf16 (the sum l took the exact values); for the row's largest one (the same fma +
+  // exp2 as in the tile, so the same value) add back what the rounding dropped, r = p - bf16(p),
+  // times its value row. Without this, a row dominated by one column whose score came after the
+  // reference tile is off by up to 2^-9 of that column's values. The lane pair first agrees on the
+  // row's best column; the pair's two waves then swap their own rows' (r, column) so each can
+  // correct its output half of both blocks.
+  float r_own;
+  int col_own;
+  {
+    const auto rs = __builtin_amdgcn_permlane32_swap(__float_as_uint(best_raw), __float_as_uint(best_raw), false,
+                                                     false);
+    const auto cs = __builtin_amdgcn_permlane32_swap((unsigned)best_col, (unsigned)best_col, false, false);
+    const float ra = __uint_as_float(rs[0]), rb = __uint_as_float(rs[1]);
+    const int ca = (int)cs[0], cb = (int)cs[1];
+    const bool take_b = rb > ra || (rb == ra && cb < ca);
+    const float top = take_b ? rb : ra;
+    col_own = take_b ? cb : ca;
+    const float base = m_ref == -INFINITY ? 0.0f : m_ref;
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(top, x.scale_log2, -base));
+    r_own = top == -INFINITY ? 0.0f : p - (float)(__bf16)p;
+  }
+  float* const xch = reinterpret_cast<float*>(lds.s);
+  if (lane < 32) {
+    xch[(w * 32 + lane) * 2] = r_own;
+    xch[(w * 32 + lane) * 2 + 1] = __int_as_float(col_own);
+  }
+  lds_barrier();
+  const float r_par = xch[((w ^ 1) * 32 + (lane & 31)) * 2];
+  const int col_par = __float_as_int(xch[((w ^ 1) * 32 + (lane & 31)) * 2 + 1]);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float r = i == 0 ? r_own : r_par;
+    const int c = i == 0 ? col_own : col_par;
+    if (set_row(i) < R && r != 0.0f) {
+      int slot = c < P ? kv_indices[kv_start + c] : out_cache_loc[(size_t)b * q_len + (c - P)];
+      slot = min(max(slot, 0), a.N - 1);
+      const uint8_t* vrow = kv_pool + (size_t)slot * kRowBytes;
+#pragma unroll
+      for (int eb = 0; eb < kHalfEBlocks; ++eb) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e0 = 256 * hf + 32 * eb + 8 * j + 4 * g;
+          const uint2 v = *reinterpret_cast<const uint2*>(vrow + 2 * e0);
+          oacc[i][eb][4 * j + 0] += r * __uint_as_float(v.x << 16);
+          oacc[i][eb][4 * j + 1] += r * __uint_as_float(v.x & 0xFFFF0000u);
+          oacc[i][eb][4 * j + 2] += r * __uint_as_float(v.y << 16);
+          oacc[i][eb][4 * j + 3] += r * __uint_as_float(v.y & 0xFFFF0000u);
+        }
+      }
+    }
   }
 
   // ---- partial write: (m_ref, l) of the own block and this wave's half of both blocks'
@@ -634,17 +726,183 @@ verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restric
   if (own_row < R && g == 0) ws_ml[part + own_row] = make_float2(m_ref, l_row);
 }
 
+#define PARTIAL_LDS_DECL                                                          \
+  __shared__ __attribute__((aligned(16))) uint8_t lds_kv[kBufs * kTileBytes];     \
+  __shared__ __attribute__((aligned(16))) uint8_t lds_s[kWaves * kSXchgBytes];    \
+  __shared__ __attribute__((aligned(16))) uint8_t lds_p[kWaves * kPXchgBytes];    \
+  __shared__ __attribute__((aligned(16))) uint8_t lds_meta[kWaves * kMetaStages * kMetaBytes]; \
+  __shared__ int lds_over[kWaves];                                                \
+  const PartialLds lds = {lds_kv, lds_s, lds_p, lds_meta, lds_over};
+
+// Per-request splits: workgroup -> (request b, split s, row tile) by decode_unit; split s of request
+// b covers columns [s*chunk, min(L_b, (s+1)*chunk)) with chunk = ceil(L_b / nsplit) rounded up to the
+// tile, and writes partial row block (b*nsplit + s)*R. An empty split writes (m = -inf, l = 0).
+__global__ void __launch_bounds__(kWaves * 64, 1)
+verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restrict__ q_rope,
+                      const uint8_t* __restrict__ kv_pool, int N,
+                      const int32_t* __restrict__ kv_indptr, const int32_t* __restrict__ kv_indices,
+                      const int32_t* __restrict__ out_cache_loc,
+                      const uint8_t* __restrict__ custom_mask,
+                      const int32_t* __restrict__ mask_indptr, int B, int q_len, int H,
+                      float scale_log2, int nsplit, int n_rt, float2* __restrict__ ws_ml,
+                      float* __restrict__ ws_acc) {
+  PARTIAL_LDS_DECL
+  const PartialArgs a = {q_nope, q_rope, kv_pool, N, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
+                         B, q_len, H, scale_log2, ws_ml, ws_acc};
+  const Split sp = decode_unit(a.B, nsplit, n_rt);
+  if (!sp.valid) return;
+  const int b = sp.b, s = sp.s;
+  const int R = a.q_len * a.H;
+  // split bounds from the actual lengths (empty splits leave at once)
+  const int L = max(a.kv_indptr[b + 1] - a.kv_indptr[b], 0) + a.q_len;
+  int chunk = (L + nsplit - 1) / nsplit;
+  chunk = (chunk + kTile - 1) / kTile * kTile;
+  const int c_begin = s * chunk;
+  const int c_end = min(L, c_begin + chunk);
+  const size_t part = ((size_t)b * nsplit + s) * R;
+  run_split(a, lds, b, c_begin, c_end, sp.rt, part);
+}
+
+// ---- Balanced partition of the batch. Request b has T_b = ceil(L_b / 32) column tiles. With a
+// budget of `units` splits for the whole batch (units >= B), the plan takes the smallest split size C
+// (in tiles) for which sum_b ceil(T_b / C) <= units, gives request b n_b = ceil(T_b / C) splits and
+// cuts its tiles evenly: split s covers tiles [floor(s T_b / n_b), floor((s+1) T_b / n_b)). This
+// minimises the largest split, so a ragged batch spreads over a fixed grid in near-equal pieces
+// (a short request gets one split, a long one many) instead of nsplit splits per request. Splits are
+// numbered request after request: split_start[b] = sum_{b' < b} n_b', and the partial of split
+// split_start[b] + s is partial row block (split_start[b] + s) * R. Splits never straddle requests, so
+// a workgroup keeps one request's query rows, exactly like the per-request kernel.
+constexpr int kPlanThreads = 1024;
+
+__device__ __forceinline__ long long plan_block_sum(long long x, long long* red) {
+  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  long long t = 0;
+  for (int k = 0; k < kPlanThreads / 64; ++k) t += red[k];
+  return t;
+}
+
+// One workgroup: split_start [B + 1] and req_of_split [units] (-1 for unused splits).
+__global__ void __launch_bounds__(kPlanThreads)
+verify_plan_kernel(const int32_t* __restrict__ kv_indptr, int B, int q_len, int units,
+                   int* __restrict__ split_start, int* __restrict__ req_of_split) {
+  __shared__ int tiles[MLA_VERIFY_BALANCED_MAX_B];
+  __shared__ int start_s[MLA_VERIFY_BALANCED_MAX_B + 1];
+  __shared__ long long red[kPlanThreads / 64];
+  __shared__ int wave_tot[kPlanThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  long long tmax = 1;
+  for (int b = tid; b < B; b += kPlanThreads) {
+    const long long L = max((long long)kv_indptr[b + 1] - (long long)kv_indptr[b], 0LL) + q_len;
+    const int t = (int)((L + kTile - 1) / kTile);
+    tiles[b] = t;
+    tmax = max(tmax, (long long)t);
+  }
+  // largest T_b (a block max through the sum helper's layout)
+  for (int d = 32; d >= 1; d >>= 1) tmax = max(tmax, (long long)__shfl_xor(tmax, d, 64));
+  __syncthreads();
+  if (lane == 0) red[wave] = tmax;
+  __syncthreads();
+  long long hi = 1;
+  for (int k = 0; k < kPlanThreads / 64; ++k) hi = max(hi, red[k]);
+  // smallest C in [1, hi] with sum ceil(T_b / C) <= units (C = hi gives B splits, and B <= units)
+  long long lo = 1;
+  while (lo < hi) {
+    const long long mid = (lo + hi) / 2;
+    long long cnt = 0;
+    for (int b = tid; b < B; b += kPlanThreads) cnt += (tiles[b] + mid - 1) / mid;
+    cnt = plan_block_sum(cnt, red);
+    if (cnt <= units) hi = mid; else lo = mid + 1;
+  }
+  const long long C = lo;
+  // split_start: running sum of n_b
+  int carry = 0;
+  if (tid == 0) start_s[0] = 0;
+  for (int b0 = 0; b0 < B; b0 += kPlanThreads) {
+    const int b = b0 + tid;
+    int x = b < B ? (int)((tiles[b] + C - 1) / C) : 0;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d, 64);
+      if (lane >= d) x += y;
+    }
+    if (lane == 63) wave_tot[wave] = x;
+    __syncthreads();
+    int before = 0, tot = 0;
+    for (int k = 0; k < kPlanThreads / 64; ++k) {
+      const int t = wave_tot[k];
+      if (k < wave) before += t;
+      tot += t;
+    }
+    if (b < B) start_s[b + 1] = carry + before + x;
+    carry += tot;
+    __syncthreads();
+  }
+  for (int b = tid; b <= B; b += kPlanThreads) split_start[b] = start_s[b];
+  for (int j = tid; j < units; j += kPlanThreads) {
+    int l = 0, h = B;  // the last b with start_s[b] <= j
+    while (h - l > 1) {
+      const int mid = (l + h) >> 1;
+      if (start_s[mid] <= j) l = mid; else h = mid;
+    }
+    req_of_split[j] = j < start_s[B] ? l : -1;
+  }
+}
+
+// Workgroup -> (split j, row tile): split j on XCD j % 8 with all its row tiles (they read the same KV
+// rows). The grid is 8 * ceil(units / 8) * n_rt; splits the plan leaves unused exit at once.
+__global__ void __launch_bounds__(kWaves * 64, 1)
+verify_partial_balanced_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restrict__ q_rope,
+                               const uint8_t* __restrict__ kv_pool, int N,
+                               const int32_t* __restrict__ kv_indptr, const int32_t* __restrict__ kv_indices,
+                               const int32_t* __restrict__ out_cache_loc,
+                               const uint8_t* __restrict__ custom_mask,
+                               const int32_t* __restrict__ mask_indptr, int B, int q_len, int H,
+                               float scale_log2, int units, int n_rt, const int* __restrict__ split_start,
+                               const int* __restrict__ req_of_split, float2* __restrict__ ws_ml,
+                               float* __restrict__ ws_acc) {
+  PARTIAL_LDS_DECL
+  const PartialArgs a = {q_nope, q_rope, kv_pool, N, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
+                         B, q_len, H, scale_log2, ws_ml, ws_acc};
+  const int xcd = (int)(blockIdx.x % 8), k = (int)(blockIdx.x / 8);
+  const int j = xcd + 8 * (k / n_rt), rt = k % n_rt;
+  if (j >= units) return;
+  const int b = req_of_split[j];
+  if (b < 0) return;
+  const int s0 = split_start[b];
+  const int n_b = split_start[b + 1] - s0, s = j - s0;
+  const int L = max(kv_indptr[b + 1] - kv_indptr[b], 0) + q_len;
+  const long long T_b = (L + kTile - 1) / kTile;
+  const int c_begin = (int)((long long)s * T_b / n_b) * kTile;
+  const int c_end = min(L, (int)((long long)(s + 1) * T_b / n_b) * kTile);
+  run_split(a, lds, b, c_begin, c_end, rt, (size_t)j * (q_len * H));
+}
+
 // One wave per query row (b, r): weights w_s = 2^(m_s - M) over the non-empty partials,
 // out = sum w_s acc_s / sum w_s l_s, lse = (M + log2 sum w_s l_s) * ln 2. Lane k owns output
 // columns [8k, 8k+8); the splits are walked 8 at a time with all their loads issued together.
+// kBalanced: the partials of request b are blocks split_start[b] .. split_start[b+1] - 1 (the plan);
+// otherwise the nsplit blocks b * nsplit .. b * nsplit + nsplit - 1.
+template <bool kBalanced>
 __global__ void __launch_bounds__(256)
 verify_combine_kernel(const float2* __restrict__ ws_ml, const float* __restrict__ ws_acc, int B, int R,
-                      int nsplit, __bf16* __restrict__ out, float* __restrict__ lse) {
+                      int nsplit_or_units, const int* __restrict__ split_start, __bf16* __restrict__ out,
+                      float* __restrict__ lse) {
   const int lane = threadIdx.x & 63;
   const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);  // global row index b*R + r
   if (row >= (long)B * R) return;
   const long b = row / R, r = row % R;
-  const float2* ml = ws_ml + (size_t)b * nsplit * R + r;
+  size_t first;
+  int nsplit;
+  if constexpr (kBalanced) {
+    first = (size_t)split_start[b];
+    nsplit = split_start[b + 1] - split_start[b];
+  } else {
+    nsplit = nsplit_or_units;
+    first = (size_t)b * nsplit;
+  }
+  const float2* ml = ws_ml + first * R + r;
   // M over the splits: lane s reads split s (and s + 64, ...), then a wave max
   float M = -INFINITY;
   for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, ml[(size_t)s * R].x);
@@ -658,7 +916,7 @@ verify_combine_kernel(const float2* __restrict__ ws_ml, const float* __restrict_
   }
   f32x4 acc0 = {}, acc1 = {};
   float den = 0.0f;
-  const float* base = ws_acc + ((size_t)b * nsplit * R + r) * kLatent + lane * 8;
+  const float* base = ws_acc + (first * R + r) * kLatent + lane * 8;
   const size_t split_stride = (size_t)R * kLatent;
   constexpr int kU = 8;
   for (int s0 = 0; s0 < nsplit; s0 += kU) {
@@ -711,12 +969,36 @@ bool sizes_ok(int B, int q_len, int H) {
   return rows <= (1LL << 24) && (long long)B * rows <= (1LL << 30);
 }
 
+// Balanced workspace: the plan (split_start int32 [B + 1], req_of_split int32 [units]), then (m, l)
+// and accumulators for `units` partial row blocks, each region 256-byte aligned.
+struct BalancedLayout {
+  size_t plan_bytes, ml_bytes, acc_bytes;
+};
+
+BalancedLayout balanced_layout(int B, int q_len, int H, int units) {
+  const size_t rows = (size_t)units * q_len * H;
+  return {align_up((size_t)(B + 1 + units) * sizeof(int), MLA_VERIFY_WORKSPACE_ALIGN),
+          align_up(rows * sizeof(float2), MLA_VERIFY_WORKSPACE_ALIGN),
+          align_up(rows * kLatent * sizeof(float), MLA_VERIFY_WORKSPACE_ALIGN)};
+}
+
+bool balanced_sizes_ok(int B, int q_len, int H, int units) {
+  return sizes_ok(B, q_len, H) && B <= MLA_VERIFY_BALANCED_MAX_B && units >= B && units <= MLA_VERIFY_MAX_UNITS &&
+         (long long)units * q_len * H <= (1LL << 30);
+}
+
 }  // namespace
 
 extern "C" size_t mla_verify_attn_workspace_size(int B, int q_len, int H, int nsplit) {
   if (!sizes_ok(B, q_len, H) || nsplit < 1 || nsplit > MLA_VERIFY_MAX_NSPLIT) return 0;
   const WorkspaceLayout lay = workspace_layout(B, q_len, H, nsplit);
   return lay.ml_bytes + lay.acc_bytes;
+}
+
+extern "C" size_t mla_verify_attn_balanced_workspace_size(int B, int q_len, int H, int units) {
+  if (!balanced_sizes_ok(B, q_len, H, units)) return 0;
+  const BalancedLayout lay = balanced_layout(B, q_len, H, units);
+  return lay.plan_bytes + lay.ml_bytes + lay.acc_bytes;
 }
 
 extern "C" const char* mla_verify_status_string(int status) {
@@ -761,18 +1043,71 @@ int launch_partial(const void* q_nope, const void* q_rope, const void* kv_pool, 
   const int n_rt = (ws.R + kRowsPerWG - 1) / kRowsPerWG;
   const long long grid = ((long long)B * nsplit + 7) / 8 * 8 * n_rt;
   if (grid > INT32_MAX) return MLA_VERIFY_ERR_SHAPE;
-  const float scale_log2 = scale * 1.44269504088896340736f;
-  hipLaunchKernelGGL(verify_partial_kernel, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream,
-                     static_cast<const __bf16*>(q_nope), static_cast<const __bf16*>(q_rope),
-                     static_cast<const uint8_t*>(kv_pool), (int)N, kv_indptr, kv_indices, out_cache_loc,
-                     custom_mask, mask_indptr, B, q_len, H, scale_log2, nsplit, n_rt, ws.ws_ml, ws.ws_acc);
+  const PartialArgs a = {static_cast<const __bf16*>(q_nope), static_cast<const __bf16*>(q_rope),
+                         static_cast<const uint8_t*>(kv_pool), (int)N, kv_indptr, kv_indices, out_cache_loc,
+                         custom_mask, mask_indptr, B, q_len, H, scale * 1.44269504088896340736f,
+                         ws.ws_ml, ws.ws_acc};
+  hipLaunchKernelGGL(verify_partial_kernel, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, a.q_nope, a.q_rope,
+                     a.kv_pool, a.N, a.kv_indptr, a.kv_indices, a.out_cache_loc, a.custom_mask, a.mask_indptr, a.B,
+                     a.q_len, a.H, a.scale_log2, nsplit, n_rt, a.ws_ml, a.ws_acc);
   return hipGetLastError() == hipSuccess ? MLA_VERIFY_OK : MLA_VERIFY_ERR_LAUNCH;
 }
 
 int launch_combine(const Launch& ws, int B, int nsplit, void* out, float* lse, hipStream_t stream) {
   const long long crows = (long long)B * ws.R;
-  hipLaunchKernelGGL(verify_combine_kernel, dim3((unsigned)((crows + 3) / 4)), dim3(256), 0, stream, ws.ws_ml,
-                     ws.ws_acc, B, ws.R, nsplit, static_cast<__bf16*>(out), lse);
+  hipLaunchKernelGGL(verify_combine_kernel<false>, dim3((unsigned)((crows + 3) / 4)), dim3(256), 0, stream, ws.ws_ml,
+                     ws.ws_acc, B, ws.R, nsplit, nullptr, static_cast<__bf16*>(out), lse);
+  return hipGetLastError() == hipSuccess ? MLA_VERIFY_OK : MLA_VERIFY_ERR_LAUNCH;
+}
+
+struct BalancedLaunch {
+  int* split_start;
+  int* req_of_split;
+  float2* ws_ml;
+  float* ws_acc;
+  int R;
+};
+
+int check_balanced(int B, int q_len, int H, int units, const void* workspace, size_t workspace_bytes) {
+  if (!sizes_ok(B, q_len, H) || B > MLA_VERIFY_BALANCED_MAX_B) return MLA_VERIFY_ERR_SHAPE;
+  if (units < B || units > MLA_VERIFY_MAX_UNITS) return MLA_VERIFY_ERR_NSPLIT;
+  if (!balanced_sizes_ok(B, q_len, H, units)) return MLA_VERIFY_ERR_SHAPE;
+  const size_t need = mla_verify_attn_balanced_workspace_size(B, q_len, H, units);
+  if (!workspace || ((uintptr_t)workspace % MLA_VERIFY_WORKSPACE_ALIGN) != 0 || workspace_bytes < need)
+    return MLA_VERIFY_ERR_WORKSPACE;
+  return MLA_VERIFY_OK;
+}
+
+BalancedLaunch balanced_workspace(void* workspace, int B, int q_len, int H, int units) {
+  const BalancedLayout lay = balanced_layout(B, q_len, H, units);
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  return {reinterpret_cast<int*>(w), reinterpret_cast<int*>(w) + (B + 1),
+          reinterpret_cast<float2*>(w + lay.plan_bytes), reinterpret_cast<float*>(w + lay.plan_bytes + lay.ml_bytes),
+          q_len * H};
+}
+
+int launch_balanced_partial(const void* q_nope, const void* q_rope, const void* kv_pool, int64_t N,
+                            const int32_t* kv_indptr, const int32_t* kv_indices, const int32_t* out_cache_loc,
+                            const uint8_t* custom_mask, const int32_t* mask_indptr, int B, int q_len, int H,
+                            float scale, int units, const BalancedLaunch& ws, hipStream_t stream) {
+  const int n_rt = (ws.R + kRowsPerWG - 1) / kRowsPerWG;
+  const long long grid = ((long long)units + 7) / 8 * 8 * n_rt;
+  if (grid > INT32_MAX) return MLA_VERIFY_ERR_SHAPE;
+  hipLaunchKernelGGL(verify_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, kv_indptr, B, q_len, units,
+                     ws.split_start, ws.req_of_split);
+  if (hipGetLastError() != hipSuccess) return MLA_VERIFY_ERR_LAUNCH;
+  hipLaunchKernelGGL(verify_partial_balanced_kernel, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream,
+                     static_cast<const __bf16*>(q_nope), static_cast<const __bf16*>(q_rope),
+                     static_cast<const uint8_t*>(kv_pool), (int)N, kv_indptr, kv_indices, out_cache_loc, custom_mask,
+                     mask_indptr, B, q_len, H, scale * 1.44269504088896340736f, units, n_rt,
+                     (const int*)ws.split_start, (const int*)ws.req_of_split, ws.ws_ml, ws.ws_acc);
+  return hipGetLastError() == hipSuccess ? MLA_VERIFY_OK : MLA_VERIFY_ERR_LAUNCH;
+}
+
+int launch_balanced_combine(const BalancedLaunch& ws, int B, int units, void* out, float* lse, hipStream_t stream) {
+  const long long crows = (long long)B * ws.R;
+  hipLaunchKernelGGL(verify_combine_kernel<true>, dim3((unsigned)((crows + 3) / 4)), dim3(256), 0, stream, ws.ws_ml,
+                     ws.ws_acc, B, ws.R, units, (const int*)ws.split_start, static_cast<__bf16*>(out), lse);
   return hipGetLastError() == hipSuccess ? MLA_VERIFY_OK : MLA_VERIFY_ERR_LAUNCH;
 }
 
@@ -824,4 +1159,49 @@ extern "C" int mla_verify_attn(const void* q_nope, const void* q_rope, const voi
                       q_len, H, scale, nsplit, ws, stream);
   if (rc != MLA_VERIFY_OK) return rc;
   return launch_combine(ws, B, nsplit, out, lse, stream);
+}
+
+extern "C" int mla_verify_attn_balanced_partial(const void* q_nope, const void* q_rope, const void* kv_pool,
+                                                int64_t N, const int32_t* kv_indptr, const int32_t* kv_indices,
+                                                const int32_t* out_cache_loc, const uint8_t* custom_mask,
+                                                const int32_t* mask_indptr, int B, int q_len, int H, float scale,
+                                                int units, void* workspace, size_t workspace_bytes,
+                                                hipStream_t stream) {
+  if (inputs_null(q_nope, q_rope, kv_pool, kv_indptr, out_cache_loc, custom_mask, mask_indptr))
+    return MLA_VERIFY_ERR_NULL;
+  if (!sizes_ok(B, q_len, H) || N < 1 || N > INT32_MAX || !(scale > 0.0f) || !isfinite(scale))
+    return MLA_VERIFY_ERR_SHAPE;
+  const int rc = check_balanced(B, q_len, H, units, workspace, workspace_bytes);
+  if (rc != MLA_VERIFY_OK) return rc;
+  return launch_balanced_partial(q_nope, q_rope, kv_pool, N, kv_indptr, kv_indices, out_cache_loc, custom_mask,
+                                 mask_indptr, B, q_len, H, scale, units,
+                                 balanced_workspace(workspace, B, q_len, H, units), stream);
+}
+
+extern "C" int mla_verify_attn_balanced_combine(const void* workspace, size_t workspace_bytes, int B, int q_len,
+                                                int H, int units, void* out, float* lse, hipStream_t stream) {
+  if (!out || !lse) return MLA_VERIFY_ERR_NULL;
+  const int rc = check_balanced(B, q_len, H, units, workspace, workspace_bytes);
+  if (rc != MLA_VERIFY_OK) return rc;
+  return launch_balanced_combine(balanced_workspace(const_cast<void*>(workspace), B, q_len, H, units), B, units, out,
+                                 lse, stream);
+}
+
+extern "C" int mla_verify_attn_balanced(const void* q_nope, const void* q_rope, const void* kv_pool, int64_t N,
+                                        const int32_t* kv_indptr, const int32_t* kv_indices,
+                                        const int32_t* out_cache_loc, const uint8_t* custom_mask,
+                                        const int32_t* mask_indptr, int B, int q_len, int H, float scale, int units,
+                                        void* workspace, size_t workspace_bytes, void* out, float* lse,
+                                        hipStream_t stream) {
+  if (inputs_null(q_nope, q_rope, kv_pool, kv_indptr, out_cache_loc, custom_mask, mask_indptr) || !out || !lse)
+    return MLA_VERIFY_ERR_NULL;
+  if (!sizes_ok(B, q_len, H) || N < 1 || N > INT32_MAX || !(scale > 0.0f) || !isfinite(scale))
+    return MLA_VERIFY_ERR_SHAPE;
+  int rc = check_balanced(B, q_len, H, units, workspace, workspace_bytes);
+  if (rc != MLA_VERIFY_OK) return rc;
+  const BalancedLaunch ws = balanced_workspace(workspace, B, q_len, H, units);
+  rc = launch_balanced_partial(q_nope, q_rope, kv_pool, N, kv_indptr, kv_indices, out_cache_loc, custom_mask,
+                               mask_indptr, B, q_len, H, scale, units, ws, stream);
+  if (rc != MLA_VERIFY_OK) return rc;
+  return launch_balanced_combine(ws, B, units, out, lse, stream);
 }

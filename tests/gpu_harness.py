@@ -45,21 +45,24 @@ class DeviceCall:
         self.lse = torch.empty((inp.B, inp.q_len, inp.H), dtype=torch.float32, device=self.dev)
         self.ws = None
 
-    def workspace(self, nsplit, poison=True):
-        need = pkg.workspace_size(self.inp.B, self.inp.q_len, self.inp.H, nsplit)
+    def workspace(self, nsplit, poison=True, balanced=False):
+        size = pkg.balanced_workspace_size if balanced else pkg.workspace_size
+        need = size(self.inp.B, self.inp.q_len, self.inp.H, nsplit)
+        assert need > 0
         if self.ws is None or self.ws.numel() < need:
             self.ws = torch.empty(need, dtype=torch.uint8, device=self.dev)
         if poison:
             self.ws.fill_(0xFF)  # NaN in every float: a partial read before it is written shows up
         return self.ws
 
-    def run(self, nsplit, poison=True, stream=None):
-        ws = self.workspace(nsplit, poison)
+    def run(self, nsplit, poison=True, stream=None, balanced=False):
+        """One call; balanced=True runs the balanced partition with nsplit as its split budget."""
+        ws = self.workspace(nsplit, poison, balanced)
         self.out.fill_(float("nan"))
         self.lse.fill_(float("nan"))
         pkg.verify_attn(self.q_nope, self.q_rope, self.pool, self.kv_indptr, self.kv_indices, self.out_cache_loc,
                         self.custom_mask, self.mask_indptr, self.inp.scale, nsplit, ws, self.out, self.lse,
-                        stream=stream)
+                        stream=stream, balanced=balanced)
         return self.out, self.lse
 
     def host(self):

@@ -24,7 +24,9 @@ def test_library_exports_every_declared_function():
     names = _declared_functions()
     assert set(names) == {"mla_verify_attn", "mla_verify_attn_partial", "mla_verify_attn_combine",
                           "mla_verify_attn_workspace_size", "mla_verify_status_string",
-                          "mla_verify_tree_mask", "mla_verify_kv_compact"}
+                          "mla_verify_tree_mask", "mla_verify_kv_compact",
+                          "mla_verify_attn_balanced", "mla_verify_attn_balanced_partial",
+                          "mla_verify_attn_balanced_combine", "mla_verify_attn_balanced_workspace_size"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -111,3 +113,25 @@ def test_kv_compact_validates_before_any_hip_call():
         assert pkg.kv_compact_raw(**{**ok, f: None}) == -1, f
     for kw in (dict(B=0), dict(B=4097), dict(N=0), dict(N=2**31), dict(kv_pool=FAKE + 8)):
         assert pkg.kv_compact_raw(**{**ok, **kw}) == -2, kw
+
+
+def test_balanced_workspace_size_and_validation():
+    rows = 40 * 16 * 64
+    plan = -(-(5 + 40) * 4 // 256) * 256
+    expect = plan + -(-rows * 8 // 256) * 256 + -(-rows * 2048 // 256) * 256
+    assert pkg.balanced_workspace_size(4, 16, 64, 40) == expect
+    assert pkg.balanced_workspace_size(4, 16, 64, 3) == 0          # fewer units than requests
+    assert pkg.balanced_workspace_size(4, 16, 64, 4097) == 0
+    assert pkg.balanced_workspace_size(4097, 1, 1, 4097) == 0
+    ws = pkg.balanced_workspace_size(2, 9, 8, 8)
+    base = dict(q_nope=FAKE, q_rope=FAKE, kv_pool=FAKE, N=100, kv_indptr=FAKE, kv_indices=FAKE,
+                out_cache_loc=FAKE, custom_mask=FAKE, mask_indptr=FAKE, B=2, q_len=9, H=8, scale=0.07, units=8,
+                workspace=0x100000, workspace_bytes=ws, out=FAKE, lse=FAKE, stream=None)
+    assert pkg.balanced_raw(**{**base, "out": None}) == -1
+    assert pkg.balanced_raw(**{**base, "units": 1}) == -3
+    assert pkg.balanced_raw(**{**base, "units": 4097}) == -3
+    assert pkg.balanced_raw(**{**base, "B": 4097}) == -2
+    assert pkg.balanced_raw(**{**base, "workspace_bytes": ws - 1}) == -4
+    assert pkg.balanced_raw(**{**base, "workspace": 0x100010}) == -4
+    assert pkg.balanced_combine_raw(0x100000, ws, 2, 9, 8, 8, None, FAKE, None) == -1
+    assert pkg.balanced_combine_raw(0x100000, ws - 1, 2, 9, 8, 8, FAKE, FAKE, None) == -4

@@ -1,0 +1,132 @@
+"""GPU parity of the balanced partition (mla_verify_attn_balanced) against the CPU oracles."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_harness import DeviceCall, compare, sample_rows
+from oracle import schedule as S
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [
+    # seed, prefixes, q_len, H
+    (1, (256,), 9, 8),
+    (3, (0,), 5, 3),
+    (4, (100, 0, 37), 4, 2),
+    (5, (500,), 1, 64),
+    (6, (70, 300), 16, 16),
+    (9, (3000, 12), 9, 8),
+    (10, (31, 32, 33), 3, 5),
+    (13, (300,), 6, 48),
+    (14, (4000, 10, 700, 64, 2500), 9, 16),
+]
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _oracle_full(inp):
+    pool, ki, oc = W.compact_inputs(inp)
+    return oracle.attn(*oracle.inputs_args(inp, pool, ki, oc))
+
+
+@pytest.mark.parametrize("seed,prefixes,q_len,H", SHAPES)
+@pytest.mark.parametrize("extra", [0, 1, 7, 61])
+def test_balanced_parity(seed, prefixes, q_len, H, extra):
+    units = len(prefixes) + extra
+    _say(f"[balanced] seed={seed} prefixes={prefixes} q_len={q_len} H={H} units={units}")
+    inp = W.make_custom(np.random.default_rng(seed), prefixes, q_len, H)
+    call = DeviceCall(inp)
+    call.run(units, balanced=True)
+    got_out, got_lse = call.host()
+    ref_out, ref_lse = _oracle_full(inp)
+    compare(got_out, got_lse, ref_out, ref_lse, f"balanced seed {seed} units {units}")
+
+
+@pytest.mark.parametrize("seed,prefixes,q_len,H", SHAPES[:6])
+def test_one_split_per_request_matches_nsplit_1_bit_exact(seed, prefixes, q_len, H):
+    inp = W.make_custom(np.random.default_rng(seed), prefixes, q_len, H)
+    call = DeviceCall(inp)
+    call.run(1)
+    a_out, a_lse = call.out.clone(), call.lse.clone()
+    call.run(len(prefixes), balanced=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a_out.view(torch.int16), call.out.view(torch.int16))
+    assert torch.equal(a_lse, call.lse)
+
+
+@pytest.mark.parametrize("prefixes,q_len,units", [((4096, 32768, 120000, 185000), 16, 32),
+                                                  ((4096, 32768, 120000, 185000), 16, 100),
+                                                  ((5, 0, 700, 64, 2500, 1), 9, 6),
+                                                  ((5, 0, 700, 64, 2500, 1), 9, 4096)])
+def test_plan_bit_exact(prefixes, q_len, units):
+    """The plan the device writes into the workspace equals the oracle plan (index work: exact)."""
+    B = len(prefixes)
+    ip = np.concatenate([[0], np.cumsum(prefixes)]).astype(np.int32)
+    dev = torch.device("cuda:0")
+    import speculative_decoding_mla_split_amd as pkg
+    ws = torch.full((pkg.balanced_workspace_size(B, q_len, 1, units),), 0xFF, dtype=torch.uint8, device=dev)
+    kv_indptr = torch.from_numpy(ip).to(dev)
+    # a tiny pool and zero queries: only the plan is checked here
+    pool = torch.zeros((8, 576), dtype=torch.bfloat16, device=dev)
+    kv_idx = torch.zeros(max(1, int(ip[-1])), dtype=torch.int32, device=dev)
+    occ = torch.zeros(B * q_len, dtype=torch.int32, device=dev)
+    mask_ip = torch.from_numpy(np.concatenate([[0], np.cumsum([q_len * (p + q_len) for p in prefixes])])
+                               .astype(np.int32)).to(dev)
+    mask = torch.ones(int(mask_ip[-1].item()), dtype=torch.uint8, device=dev)
+    q_nope = torch.zeros((B, q_len, 1, 512), dtype=torch.bfloat16, device=dev)
+    q_rope = torch.zeros((B, q_len, 1, 64), dtype=torch.bfloat16, device=dev)
+    _say(f"[plan] prefixes={prefixes} units={units}")
+    rc = pkg.balanced_partial_raw(q_nope.data_ptr(), q_rope.data_ptr(), pool.data_ptr(), 8, kv_indptr.data_ptr(),
+                                  kv_idx.data_ptr(), occ.data_ptr(), mask.data_ptr(), mask_ip.data_ptr(), B, q_len, 1,
+                                  0.07, units, ws.data_ptr(), ws.numel(), None)
+    assert rc == 0
+    torch.cuda.synchronize()
+    plan = ws[: 4 * (B + 1 + units)].cpu().numpy().view(np.int32)
+    split_start, req, _ = S.balanced_plan(ip, B, q_len, units)
+    assert plan[:B + 1].tolist() == split_start
+    assert plan[B + 1:].tolist() == req
+
+
+@pytest.mark.parametrize("units", [32, 64])
+def test_balanced_ragged_185k_sampled(units):
+    wl = W.CONFIGS["ragged4_185k_h64"]
+    _say(f"[balanced] {wl.name} sampled rows, units {units}")
+    inp = W.make_inputs(wl)
+    call = DeviceCall(inp)
+    call.run(units, balanced=True)
+    got_out, got_lse = call.host()
+    rows = sample_rows(inp, 48)
+    pool, ki, oc = W.compact_inputs(inp)
+    ref_out, ref_lse = oracle.attn_rows(*oracle.inputs_args(inp, pool, ki, oc), rows=rows)
+    compare(got_out[rows[:, 0], rows[:, 1], rows[:, 2]], got_lse[rows[:, 0], rows[:, 1], rows[:, 2]], ref_out,
+            ref_lse, f"{wl.name} balanced {units}")
+    assert np.all(np.isfinite(got_out)) and np.all(np.isfinite(got_lse))
+
+
+def test_balanced_graph_replays_match_eager():
+    inp = W.make_custom(np.random.default_rng(40), (900, 20, 333), 9, 8)
+    call = DeviceCall(inp)
+    units = 16
+    call.run(units, balanced=True)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = call.out.clone(), call.lse.clone()
+    import speculative_decoding_mla_split_amd as pkg
+    ws = call.workspace(units, poison=False, balanced=True)
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        pkg.verify_attn(call.q_nope, call.q_rope, call.pool, call.kv_indptr, call.kv_indices, call.out_cache_loc,
+                        call.custom_mask, call.mask_indptr, inp.scale, units, ws, call.out, call.lse, stream=stream,
+                        balanced=True)
+    for k in range(4):
+        call.out.fill_(float("nan"))
+        ws.fill_(0xFF)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(call.out.view(torch.int16), ref_out.view(torch.int16)), f"replay {k}"
+        assert torch.equal(call.lse, ref_lse)
