@@ -772,75 +772,56 @@ verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restric
 // numbered request after request: split_start[b] = sum_{b' < b} n_b', and the partial of split
 // split_start[b] + s is partial row block (split_start[b] + s) * R. Splits never straddle requests, so
 // a workgroup keeps one request's query rows, exactly like the per-request kernel.
-constexpr int kPlanThreads = 1024;
+// One wave computes the plan (the batch is small and the search is a few dozen steps, so wave
+// reductions without workgroup barriers are the quickest form).
+constexpr int kPlanThreads = 64;
 
-__device__ __forceinline__ long long plan_block_sum(long long x, long long* red) {
+__device__ __forceinline__ long long wave_sum(long long x) {
   for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-  __syncthreads();
-  long long t = 0;
-  for (int k = 0; k < kPlanThreads / 64; ++k) t += red[k];
-  return t;
+  return x;
 }
 
-// One workgroup: split_start [B + 1] and req_of_split [units] (-1 for unused splits).
+// split_start [B + 1] and req_of_split [units] (-1 for unused splits).
 __global__ void __launch_bounds__(kPlanThreads)
 verify_plan_kernel(const int32_t* __restrict__ kv_indptr, int B, int q_len, int units,
                    int* __restrict__ split_start, int* __restrict__ req_of_split) {
   __shared__ int tiles[MLA_VERIFY_BALANCED_MAX_B];
   __shared__ int start_s[MLA_VERIFY_BALANCED_MAX_B + 1];
-  __shared__ long long red[kPlanThreads / 64];
-  __shared__ int wave_tot[kPlanThreads / 64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  long long tmax = 1;
-  for (int b = tid; b < B; b += kPlanThreads) {
+  const int lane = threadIdx.x;
+  int tmax = 1;
+  for (int b = lane; b < B; b += kPlanThreads) {
     const long long L = max((long long)kv_indptr[b + 1] - (long long)kv_indptr[b], 0LL) + q_len;
     const int t = (int)((L + kTile - 1) / kTile);
     tiles[b] = t;
-    tmax = max(tmax, (long long)t);
+    tmax = max(tmax, t);
   }
-  // largest T_b (a block max through the sum helper's layout)
-  for (int d = 32; d >= 1; d >>= 1) tmax = max(tmax, (long long)__shfl_xor(tmax, d, 64));
+  for (int d = 32; d >= 1; d >>= 1) tmax = max(tmax, __shfl_xor(tmax, d, 64));
   __syncthreads();
-  if (lane == 0) red[wave] = tmax;
-  __syncthreads();
-  long long hi = 1;
-  for (int k = 0; k < kPlanThreads / 64; ++k) hi = max(hi, red[k]);
-  // smallest C in [1, hi] with sum ceil(T_b / C) <= units (C = hi gives B splits, and B <= units)
-  long long lo = 1;
+  // smallest C in [1, tmax] with sum ceil(T_b / C) <= units (C = tmax gives B splits, and B <= units)
+  unsigned lo = 1, hi = (unsigned)tmax;
   while (lo < hi) {
-    const long long mid = (lo + hi) / 2;
-    long long cnt = 0;
-    for (int b = tid; b < B; b += kPlanThreads) cnt += (tiles[b] + mid - 1) / mid;
-    cnt = plan_block_sum(cnt, red);
-    if (cnt <= units) hi = mid; else lo = mid + 1;
+    const unsigned mid = (lo + hi) / 2;
+    long long cnt = 0;  // 64-bit: with C = 1 the count is the batch's whole tile total
+    for (int b = lane; b < B; b += kPlanThreads) cnt += ((unsigned)tiles[b] + mid - 1) / mid;
+    if (wave_sum(cnt) <= units) hi = mid; else lo = mid + 1;
   }
-  const long long C = lo;
-  // split_start: running sum of n_b
+  const unsigned C = lo;
+  // split_start: running sum of n_b = ceil(T_b / C)
   int carry = 0;
-  if (tid == 0) start_s[0] = 0;
+  if (lane == 0) start_s[0] = 0;
   for (int b0 = 0; b0 < B; b0 += kPlanThreads) {
-    const int b = b0 + tid;
-    int x = b < B ? (int)((tiles[b] + C - 1) / C) : 0;
+    const int b = b0 + lane;
+    int x = b < B ? (int)(((unsigned)tiles[b] + C - 1) / C) : 0;
     for (int d = 1; d < 64; d <<= 1) {
       const int y = __shfl_up(x, d, 64);
       if (lane >= d) x += y;
     }
-    if (lane == 63) wave_tot[wave] = x;
-    __syncthreads();
-    int before = 0, tot = 0;
-    for (int k = 0; k < kPlanThreads / 64; ++k) {
-      const int t = wave_tot[k];
-      if (k < wave) before += t;
-      tot += t;
-    }
-    if (b < B) start_s[b + 1] = carry + before + x;
-    carry += tot;
-    __syncthreads();
+    if (b < B) start_s[b + 1] = carry + x;
+    carry += __shfl(x, 63, 64);
   }
-  for (int b = tid; b <= B; b += kPlanThreads) split_start[b] = start_s[b];
-  for (int j = tid; j < units; j += kPlanThreads) {
+  __syncthreads();
+  for (int b = lane; b <= B; b += kPlanThreads) split_start[b] = start_s[b];
+  for (int j = lane; j < units; j += kPlanThreads) {
     int l = 0, h = B;  // the last b with start_s[b] <= j
     while (h - l > 1) {
       const int mid = (l + h) >> 1;
