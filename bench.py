@@ -379,6 +379,37 @@ def measure_kv_compact(inp, wl, stream, dev, partial_us_scattered, nsplit, balan
             "reps": reps}
 
 
+def measure_check(wk, stream, strides=(1024, 64)):
+    """Validate mode: the device reference check (mla_verify_attn_check) of the last step's output at
+    a few sample strides: time per check and the report it wrote."""
+    import math
+
+    import torch
+    pkg, inp = wk.pkg, wk.inp
+    rep = torch.zeros(pkg.REPORT_WORDS, dtype=torch.float32, device=wk.dev)
+    res = []
+    for stride in strides:
+        cws = torch.empty(pkg.check_workspace_size(inp.B, inp.q_len, inp.H, stride), dtype=torch.uint8,
+                          device=wk.dev)
+
+        def chk():
+            rc = pkg.check_raw(wk.q_nope.data_ptr(), wk.q_rope.data_ptr(), wk.pool.data_ptr(), inp.N,
+                               wk.kv_indptr.data_ptr(), wk.kv_indices.data_ptr(), wk.out_cache_loc.data_ptr(),
+                               wk.custom_mask.data_ptr(), wk.mask_indptr.data_ptr(), inp.B, inp.q_len, inp.H, inp.scale,
+                               wk.out.data_ptr(), wk.lse.data_ptr(), stride, cws.data_ptr(), cws.numel(),
+                               rep.data_ptr(), stream.cuda_stream)
+            assert rc == 0
+        us = _event_mean_us(stream, chk, 3, warmup=1)
+        r = rep.cpu().tolist()
+        rows = math.ceil(inp.B * inp.q_len * inp.H / stride)
+        cols = sum(inp.prefixes[(k // (inp.q_len * inp.H))] + inp.q_len
+                   for k in range(0, inp.B * inp.q_len * inp.H, stride))
+        res.append({"sample_stride": stride, "rows_checked": rows, "us_per_check": us,
+                    "reference_kv_bytes_read": 3 * 1152 * cols,
+                    "report": {"max_abs_out": r[0], "max_abs_lse": r[1], "rows": r[2], "bad_rows": r[3]}})
+    return res
+
+
 def step_floor_us(alg):
     return max(alg["step_bytes"] / (HBM_PEAK_GBS * 1e9), alg["flops"] / (MFMA_BF16_PEAK_TFS * 1e12)) * 1e6
 
@@ -436,6 +467,7 @@ def main():
     wall, part, comb, stepu = wk.time_steps(stream, args.steps, args.warmup)
     print(f"[bench] timed {args.steps} steps: {wall:.1f} us/step", file=sys.stderr, flush=True)
     parity = wk.parity(args.parity_rows)
+    check = None if args.no_next else measure_check(wk, stream)
     graph_us = wk.graph_us_per_step(stream, max(args.steps, 20))
     part_s, comb_s = stats(part), stats(comb)
     alg = wk.alg
@@ -460,6 +492,8 @@ def main():
         "tflops_step": alg["flops"] / (wall * 1e-6) / 1e12,
         "parity_sampled": parity,
     }
+    if check is not None:
+        result["validate_check"] = check
     main_inp = wk.inp
     del wk
     torch.cuda.empty_cache()

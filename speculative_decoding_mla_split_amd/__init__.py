@@ -55,6 +55,15 @@ def library() -> ctypes.CDLL:
         lib.mla_verify_attn_balanced_partial.restype = i32
         lib.mla_verify_attn_balanced_combine.argtypes = lib.mla_verify_attn_combine.argtypes
         lib.mla_verify_attn_balanced_combine.restype = i32
+        lib.mla_verify_attn_check.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp, i32, vp,
+                                              sz, vp, vp]
+        lib.mla_verify_attn_check_workspace_size.argtypes = [i32, i32, i32, i32]
+        lib.mla_verify_attn_check_workspace_size.restype = sz
+        lib.mla_verify_attn_validate_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+        lib.mla_verify_attn_validate_workspace_size.restype = sz
+        lib.mla_verify_attn_check.restype = i32
+        lib.mla_verify_attn_validate.argtypes = lib.mla_verify_attn.argtypes[:18] + [i32, vp, vp]
+        lib.mla_verify_attn_validate.restype = i32
         lib.mla_verify_tree_mask.argtypes = [vp, vp, i32, i32, vp, i64, vp, vp, vp]
         lib.mla_verify_tree_mask.restype = i32
         lib.mla_verify_kv_compact.argtypes = [vp, i64, vp, vp, vp, i32, vp, vp, vp]
@@ -121,6 +130,39 @@ def balanced_combine_raw(workspace, workspace_bytes, B, q_len, H, units, out, ls
     """Direct call of mla_verify_attn_balanced_combine; returns the status."""
     return int(library().mla_verify_attn_balanced_combine(workspace, int(workspace_bytes), int(B), int(q_len),
                                                           int(H), int(units), out, lse, stream))
+
+
+REPORT_MAX_OUT, REPORT_MAX_LSE, REPORT_ROWS, REPORT_BAD, REPORT_WORDS = 0, 1, 2, 3, 4
+
+
+def check_workspace_size(B: int, q_len: int, H: int, sample_stride: int) -> int:
+    """Bytes of workspace check_attn needs (0 if an argument is out of range)."""
+    return int(library().mla_verify_attn_check_workspace_size(int(B), int(q_len), int(H), int(sample_stride)))
+
+
+def validate_workspace_size(B: int, q_len: int, H: int, nsplit: int, sample_stride: int) -> int:
+    """Bytes of workspace mla_verify_attn_validate needs (0 if an argument is out of range)."""
+    return int(library().mla_verify_attn_validate_workspace_size(int(B), int(q_len), int(H), int(nsplit),
+                                                                 int(sample_stride)))
+
+
+def check_raw(q_nope, q_rope, kv_pool, N, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
+              B, q_len, H, scale, out, lse, sample_stride, workspace, workspace_bytes, report, stream) -> int:
+    """Direct call of mla_verify_attn_check with integer device addresses; returns the status."""
+    return int(library().mla_verify_attn_check(q_nope, q_rope, kv_pool, int(N), kv_indptr, kv_indices, out_cache_loc,
+                                               custom_mask, mask_indptr, int(B), int(q_len), int(H), float(scale),
+                                               out, lse, int(sample_stride), workspace, int(workspace_bytes), report,
+                                               stream))
+
+
+def validate_raw(q_nope, q_rope, kv_pool, N, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
+                 B, q_len, H, scale, nsplit, workspace, workspace_bytes, out, lse, sample_stride, report,
+                 stream) -> int:
+    """Direct call of mla_verify_attn_validate with integer device addresses; returns the status."""
+    return int(library().mla_verify_attn_validate(q_nope, q_rope, kv_pool, int(N), kv_indptr, kv_indices,
+                                                  out_cache_loc, custom_mask, mask_indptr, int(B), int(q_len),
+                                                  int(H), float(scale), int(nsplit), workspace, int(workspace_bytes),
+                                                  out, lse, int(sample_stride), report, stream))
 
 
 def tree_mask_raw(parents, kv_indptr, B, q_len, custom_mask, mask_capacity, mask_indptr, status, stream) -> int:
@@ -235,5 +277,28 @@ def compact_kv(kv_pool, kv_indptr, kv_indices, dst_start, new_kv_indices, status
         stream = torch.cuda.current_stream(kv_pool.device)
     rc = kv_compact_raw(kv_pool.data_ptr(), kv_pool.shape[0], kv_indptr.data_ptr(), kv_indices.data_ptr(),
                         dst_start.data_ptr(), B, new_kv_indices.data_ptr(), status.data_ptr(), stream.cuda_stream)
+    if rc != 0:
+        raise MlaVerifyError(rc, status_string(rc))
+
+
+def check_attn(q_nope, q_rope, kv_pool, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
+               scale: float, out, lse, report, workspace, sample_stride: int = 1, stream=None) -> None:
+    """Device-side cross-check of out/lse against the per-row reference (validate mode).
+
+    Same tensors as verify_attn; report is a float32 device tensor of REPORT_WORDS values that
+    receives (max |out - ref|, max |lse - ref|, rows checked, bad rows); workspace is a uint8 device
+    tensor of check_workspace_size(...) bytes. Nothing is synchronised.
+    """
+    import torch
+
+    B, q_len, H, _ = q_nope.shape
+    _need(report.dtype == torch.float32 and report.is_cuda and report.numel() >= REPORT_WORDS, "report")
+    _need(workspace.dtype == torch.uint8 and workspace.is_cuda, "workspace")
+    if stream is None:
+        stream = torch.cuda.current_stream(q_nope.device)
+    rc = check_raw(q_nope.data_ptr(), q_rope.data_ptr(), kv_pool.data_ptr(), kv_pool.shape[0], kv_indptr.data_ptr(),
+                   kv_indices.data_ptr() if kv_indices.numel() else None, out_cache_loc.data_ptr(),
+                   custom_mask.data_ptr(), mask_indptr.data_ptr(), B, q_len, H, scale, out.data_ptr(), lse.data_ptr(),
+                   sample_stride, workspace.data_ptr(), workspace.numel(), report.data_ptr(), stream.cuda_stream)
     if rc != 0:
         raise MlaVerifyError(rc, status_string(rc))

@@ -6,7 +6,7 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", f) for f in ("mla_verify.hip", "tree_mask.hip", "kv_compact.hip")]
+SOURCES = [os.path.join(PKG, "csrc", f) for f in ("mla_verify.hip", "tree_mask.hip", "kv_compact.hip", "verify_check.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla_verify.so")
 

@@ -26,7 +26,9 @@ def test_library_exports_every_declared_function():
                           "mla_verify_attn_workspace_size", "mla_verify_status_string",
                           "mla_verify_tree_mask", "mla_verify_kv_compact",
                           "mla_verify_attn_balanced", "mla_verify_attn_balanced_partial",
-                          "mla_verify_attn_balanced_combine", "mla_verify_attn_balanced_workspace_size"}
+                          "mla_verify_attn_balanced_combine", "mla_verify_attn_balanced_workspace_size",
+                          "mla_verify_attn_check", "mla_verify_attn_validate",
+                          "mla_verify_attn_check_workspace_size", "mla_verify_attn_validate_workspace_size"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -135,3 +137,35 @@ def test_balanced_workspace_size_and_validation():
     assert pkg.balanced_raw(**{**base, "workspace": 0x100010}) == -4
     assert pkg.balanced_combine_raw(0x100000, ws, 2, 9, 8, 8, None, FAKE, None) == -1
     assert pkg.balanced_combine_raw(0x100000, ws - 1, 2, 9, 8, 8, FAKE, FAKE, None) == -4
+
+
+def test_check_workspace_sizes():
+    # 72 rows at stride 1 -> 72 checked rows x 64 pieces x ((m, sum) + 512 accumulators)
+    pieces = 72 * 64
+    expect = -(-pieces * 8 // 256) * 256 + -(-pieces * 2048 // 256) * 256
+    assert pkg.check_workspace_size(1, 9, 8, 1) == expect
+    assert pkg.check_workspace_size(1, 9, 8, 8) < expect
+    assert pkg.check_workspace_size(1, 9, 8, 0) == 0
+    assert pkg.validate_workspace_size(1, 9, 8, 4, 1) == max(expect, pkg.workspace_size(1, 9, 8, 4))
+    assert pkg.validate_workspace_size(1, 9, 8, 0, 1) == 0
+
+
+def test_check_and_validate_validate_before_any_hip_call():
+    cws = pkg.check_workspace_size(1, 9, 8, 1)
+    base = dict(q_nope=FAKE, q_rope=FAKE, kv_pool=FAKE, N=100, kv_indptr=FAKE, kv_indices=FAKE,
+                out_cache_loc=FAKE, custom_mask=FAKE, mask_indptr=FAKE, B=1, q_len=9, H=8, scale=0.07, out=FAKE,
+                lse=FAKE, sample_stride=1, workspace=0x100000, workspace_bytes=cws, report=FAKE, stream=None)
+    for f in ("q_nope", "kv_pool", "out", "lse", "report", "mask_indptr"):
+        assert pkg.check_raw(**{**base, f: None}) == -1, f
+    for kw in (dict(sample_stride=0), dict(B=0), dict(N=0), dict(scale=float("nan"))):
+        assert pkg.check_raw(**{**base, **kw}) == -2, kw
+    assert pkg.check_raw(**{**base, "workspace_bytes": cws - 1}) == -4
+    assert pkg.check_raw(**{**base, "workspace": 0x100010}) == -4
+    ws = pkg.validate_workspace_size(1, 9, 8, 4, 1)
+    v = dict(q_nope=FAKE, q_rope=FAKE, kv_pool=FAKE, N=100, kv_indptr=FAKE, kv_indices=FAKE, out_cache_loc=FAKE,
+             custom_mask=FAKE, mask_indptr=FAKE, B=1, q_len=9, H=8, scale=0.07, nsplit=4, workspace=0x100000,
+             workspace_bytes=ws, out=FAKE, lse=FAKE, sample_stride=1, report=FAKE, stream=None)
+    assert pkg.validate_raw(**{**v, "report": None}) == -1
+    assert pkg.validate_raw(**{**v, "sample_stride": 0}) == -2
+    assert pkg.validate_raw(**{**v, "nsplit": 0}) == -3
+    assert pkg.validate_raw(**{**v, "workspace_bytes": ws - 1}) == -4
