@@ -289,9 +289,11 @@ struct Bufs {
 //   5. O^T of both blocks over the output half: each V fragment is read once and feeds two MFMAs
 // Loads: the step issues the 9 row loads of tile t+2 into ring buffer (t+2) % 3 (its previous
 // tile, t-1, every wave finished before the barrier that opened this step) and the metadata loads
-// of tile t+4, spread evenly over all three phases. A wave keeps only a few vector-memory
-// instructions in flight, and one issued into a full queue stalls the wave, so bunching the loads
-// would idle the matrix pipe; a load has about two steps to land.
+// of tile t+4, spread over the score and PV phases, where queued MFMAs keep the matrix pipe busy
+// while the wave waits to issue them (none in the softmax, which has no matrix work to hide behind).
+// A wave keeps only a few vector-memory instructions in flight, and one issued into a full queue
+// stalls the wave, so bunching the loads would idle the matrix pipe; a load has about two steps to
+// land.
 // The LDS pointers are restrict-qualified: the buffers written by direct-to-LDS loads here are
 // never the ones read here, which lets the compiler drop its own blanket wait on those loads.
 __device__ __forceinline__ void tile_step(const Ctx& x, int t, int c_begin, const Glob& gl, const Bufs& bf,
@@ -325,7 +327,8 @@ __device__ __forceinline__ void tile_step(const Ctx& x, int t, int c_begin, cons
                                        bf.kv + ((t + 2) % kBufs) * kTileBytes);
   uint8_t* const meta_dst = bf.meta + ((t + 4) % kMetaStages) * kMetaBytes;
   const int meta_c0 = tile_c0 + 4 * kTile;
-  // load slots: 0-35 follow the score MFMAs, 36-39 the softmax chunks, 40-55 the PV MFMA pairs
+  // load slots: 0-35 follow the score MFMAs, 36-39 the softmax chunks (unused), 40-55 the PV MFMA
+  // pairs
   auto loads = [&](int slot) {
     switch (slot) {  // slot is a constant after unrolling
       case 1: dma_group<0>(gat.src, gat.m0); break;
@@ -333,10 +336,10 @@ __device__ __forceinline__ void tile_step(const Ctx& x, int t, int c_begin, cons
       case 15: dma_group<2>(gat.src, gat.m0); break;
       case 22: dma_group<3>(gat.src, gat.m0); break;
       case 29: dma_group<4>(gat.src, gat.m0); break;
-      case 36: dma_group<5>(gat.src, gat.m0); break;
-      case 38: dma_group<6>(gat.src, gat.m0); break;
-      case 41: dma_group<7>(gat.src, gat.m0); break;
-      case 45: dma_group<8>(gat.src, gat.m0); break;
+      case 33: dma_group<5>(gat.src, gat.m0); break;
+      case 40: dma_group<6>(gat.src, gat.m0); break;
+      case 43: dma_group<7>(gat.src, gat.m0); break;
+      case 47: dma_group<8>(gat.src, gat.m0); break;
       case 49: issue_meta_part<0>(xm, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, meta_c0, meta_dst); break;
       case 52: issue_meta_part<1>(xm, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, meta_c0, meta_dst); break;
       case 54: issue_meta_part<2>(xm, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, meta_c0, meta_dst); break;
@@ -672,7 +675,10 @@ __device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds
     col_own = take_b ? cb : ca;
     const float base = m_ref == -INFINITY ? 0.0f : m_ref;
     const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(top, x.scale_log2, -base));
-    r_own = top == -INFINITY ? 0.0f : p - (float)(__bf16)p;
+    // a top probability under 1/32 of the row's sum moves the output by at most 2^-14 of a value
+    // row if left rounded: skip its correction (and the value-row reads)
+    const float l_pair = pair_sum(l_lane);
+    r_own = top == -INFINITY || 32.0f * p < l_pair ? 0.0f : p - (float)(__bf16)p;
   }
   float* const xch = reinterpret_cast<float*>(lds.s);
   if (lane < 32) {
