@@ -521,17 +521,25 @@ def main():
             del ow
             torch.cuda.empty_cache()
         scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        for name, lay, ns in (("16k_h64", "contiguous", 16), ("16k_h64", "scattered", 16),
-                              ("16k_h64", "scattered", 32), ("16k_h64", "scattered", 64),
-                              ("65k_h8", "scattered", 16), ("65k_h8", "scattered", 64), ("4k_h64", "scattered", 16)):
-            print(f"[bench] sweep {name} {lay} nsplit={ns}", file=sys.stderr, flush=True)
-            ow = Workload(W.CONFIGS[name], lay, ns, dev)
+        def auto_units(w):  # one workgroup per CU: the balanced schedule's default budget
+            return max(w.B, cus // -(-w.q_len * w.H // 128))
+
+        sweep = [("16k_h64", "contiguous", "per-request", 16), ("16k_h64", "scattered", "per-request", 16),
+                 ("16k_h64", "scattered", "per-request", 32), ("16k_h64", "scattered", "per-request", 64),
+                 ("65k_h8", "scattered", "per-request", 16), ("65k_h8", "scattered", "per-request", 64),
+                 ("4k_h64", "scattered", "per-request", 16)]
+        sweep += [(n, lay, "balanced", auto_units(W.CONFIGS[n])) for n, lay in
+                  (("16k_h64", "contiguous"), ("16k_h64", "scattered"), ("65k_h8", "scattered"),
+                   ("4k_h64", "scattered"))]
+        for name, lay, sched, ns in sweep:
+            print(f"[bench] sweep {name} {lay} {sched} {ns}", file=sys.stderr, flush=True)
+            ow = Workload(W.CONFIGS[name], lay, ns, dev, balanced=sched == "balanced")
             hot_wall, hp, hc, hs = ow.time_steps(stream, 30, 5)
             _, cp, cc, cs = ow.time_steps(stream, 20, 2, scrub=scrub)
             a = ow.alg
             fl = step_floor_us(a)
             others.append({
-                "workload": name, "layout": lay, "schedule": "per-request", "nsplit": ns,
+                "workload": name, "layout": lay, "schedule": sched, ("units" if sched == "balanced" else "nsplit"): ns,
                 "hot_us_per_step": hot_wall, "hot_kv_GBs": a["kv_bytes"] / (hot_wall * 1e-6) / 1e9,
                 "cold_step_us_median": stats(cs)["median"],
                 "cold_kv_GBs": a["kv_bytes"] / (stats(cs)["median"] * 1e-6) / 1e9,

@@ -10,8 +10,8 @@
 //                          tiles), shared by all 128 query rows (2 wave pairs x 64 rows). QK^T and
 //                          PV run on 32x32x16 bf16 MFMA with fp32 accumulation; the mask lookup
 //                          and online softmax happen in registers between the two.
-//   verify_combine_kernel  one wave per query row: log-sum-exp combine of the nsplit partials into
-//                          the bf16 output and the fp32 natural-log LSE.
+//   verify_combine_kernel  one workgroup per query row: log-sum-exp combine of the row's partials
+//                          into the bf16 output and the fp32 natural-log LSE.
 //
 // Layout conventions of the partial kernel (per MFMA block of 32 query rows r, columns c of one
 // tile):
@@ -866,19 +866,31 @@ verify_partial_balanced_kernel(const __bf16* __restrict__ q_nope, const __bf16* 
   run_split(a, lds, b, c_begin, c_end, rt, (size_t)j * (q_len * H));
 }
 
-// One wave per query row (b, r): weights w_s = 2^(m_s - M) over the non-empty partials,
-// out = sum w_s acc_s / sum w_s l_s, lse = (M + log2 sum w_s l_s) * ln 2. Lane k owns output
-// columns [8k, 8k+8); the splits are walked 8 at a time with all their loads issued together.
+// kWaves waves per query row (b, r): weights w_s = 2^(m_s - M) over the non-empty partials,
+// out = sum w_s acc_s / sum w_s l_s, lse = (M + log2 sum w_s l_s) * ln 2. Lane k owns output columns
+// [8k, 8k+8); wave w of a row takes splits w, w + kWaves, ..., 8 (4 with 16 waves) at a time with all
+// their loads issued together, and waves 1.. hand their sums to wave 0 through LDS. One wave per row (4 rows per
+// workgroup) suits many rows (the ragged 185k batch, 4096 rows); more waves per row keep the chip busy
+// when there are few rows and many splits (72 rows x 256 splits with one wave each left most CUs idle
+// and walked 256 splits serially: 95 us, against 26 us with four waves).
 // kBalanced: the partials of request b are blocks split_start[b] .. split_start[b+1] - 1 (the plan);
 // otherwise the nsplit blocks b * nsplit .. b * nsplit + nsplit - 1.
-template <bool kBalanced>
-__global__ void __launch_bounds__(256)
+template <int kWaves>
+constexpr int combine_block_waves() { return kWaves == 1 ? 4 : kWaves; }
+
+template <bool kBalanced, int kWaves>
+__global__ void __launch_bounds__(combine_block_waves<kWaves>() * 64)
 verify_combine_kernel(const float2* __restrict__ ws_ml, const float* __restrict__ ws_acc, int B, int R,
                       int nsplit_or_units, const int* __restrict__ split_start, __bf16* __restrict__ out,
                       float* __restrict__ lse) {
+  constexpr int kRed = kWaves > 1 ? kWaves : 2;
+  __shared__ float red_m[kRed];
+  __shared__ f32x4 red_acc[kRed - 1][2][64];
+  __shared__ float red_den[kRed - 1];
   const int lane = threadIdx.x & 63;
-  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);  // global row index b*R + r
-  if (row >= (long)B * R) return;
+  const int w = kWaves == 1 ? 0 : (int)(threadIdx.x >> 6);  // wave of the row
+  const long row = kWaves == 1 ? (long)blockIdx.x * 4 + (threadIdx.x >> 6) : (long)blockIdx.x;
+  if (row >= (long)B * R) return;  // only the one-wave form has a partial last workgroup
   const long b = row / R, r = row % R;
   size_t first;
   int nsplit;
@@ -890,28 +902,37 @@ verify_combine_kernel(const float2* __restrict__ ws_ml, const float* __restrict_
     first = (size_t)b * nsplit;
   }
   const float2* ml = ws_ml + first * R + r;
-  // M over the splits: lane s reads split s (and s + 64, ...), then a wave max
+  // M over the splits: each lane of the row's waves reads every (64 kWaves)-th split, then a max
   float M = -INFINITY;
-  for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, ml[(size_t)s * R].x);
+  for (int s = w * 64 + lane; s < nsplit; s += kWaves * 64) M = fmaxf(M, ml[(size_t)s * R].x);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  if constexpr (kWaves > 1) {
+    if (lane == 0) red_m[w] = M;
+    __syncthreads();
+    M = red_m[0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) M = fmaxf(M, red_m[k]);
+  }
   bf16x8* o = reinterpret_cast<bf16x8*>(out + (size_t)row * kLatent + lane * 8);
   if (M == -INFINITY) {
-    *o = bf16x8{};
-    if (lane == 0) lse[row] = -INFINITY;
+    if (w == 0) {
+      *o = bf16x8{};
+      if (lane == 0) lse[row] = -INFINITY;
+    }
     return;
   }
   f32x4 acc0 = {}, acc1 = {};
   float den = 0.0f;
   const float* base = ws_acc + (first * R + r) * kLatent + lane * 8;
   const size_t split_stride = (size_t)R * kLatent;
-  constexpr int kU = 8;
-  for (int s0 = 0; s0 < nsplit; s0 += kU) {
+  constexpr int kU = kWaves >= 16 ? 4 : 8;  // splits in flight per wave (the 16-wave form has 128 registers)
+  for (int s0 = w; s0 < nsplit; s0 += kWaves * kU) {
     float wgt[kU];
     f32x4 x0[kU], x1[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int s = s0 + u;
+      const int s = s0 + kWaves * u;
       const float2 st = s < nsplit ? ml[(size_t)s * R] : make_float2(-INFINITY, 0.0f);
       // empty or fully masked split: weight 0 and its accumulator is never read
       const bool live = st.x != -INFINITY;
@@ -927,6 +948,21 @@ verify_combine_kernel(const float2* __restrict__ ws_ml, const float* __restrict_
       acc1 += wgt[u] * x1[u];
     }
   }
+  if constexpr (kWaves > 1) {
+    if (w > 0) {
+      red_acc[w - 1][0][lane] = acc0;
+      red_acc[w - 1][1][lane] = acc1;
+      if (lane == 0) red_den[w - 1] = den;
+    }
+    __syncthreads();
+    if (w != 0) return;
+#pragma unroll
+    for (int k = 0; k < kWaves - 1; ++k) {
+      acc0 += red_acc[k][0][lane];
+      acc1 += red_acc[k][1][lane];
+      den += red_den[k];
+    }
+  }
   const float inv = 1.0f / den;
   bf16x8 res;
 #pragma unroll
@@ -937,6 +973,11 @@ verify_combine_kernel(const float2* __restrict__ ws_ml, const float* __restrict_
   *o = res;
   if (lane == 0) lse[row] = (M + log2f(den)) * 0.69314718055994530942f;
 }
+
+// Row counts at which the combine uses one wave per row, else four, else sixteen (enough waves to fill
+// 256 CUs either way).
+constexpr long long kCombineManyRows = 2048;
+constexpr long long kCombineFewRows = 512;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -1042,8 +1083,15 @@ int launch_partial(const void* q_nope, const void* q_rope, const void* kv_pool, 
 
 int launch_combine(const Launch& ws, int B, int nsplit, void* out, float* lse, hipStream_t stream) {
   const long long crows = (long long)B * ws.R;
-  hipLaunchKernelGGL(verify_combine_kernel<false>, dim3((unsigned)((crows + 3) / 4)), dim3(256), 0, stream, ws.ws_ml,
-                     ws.ws_acc, B, ws.R, nsplit, nullptr, static_cast<__bf16*>(out), lse);
+  if (crows >= kCombineManyRows)
+    hipLaunchKernelGGL((verify_combine_kernel<false, 1>), dim3((unsigned)((crows + 3) / 4)), dim3(256), 0, stream,
+                       ws.ws_ml, ws.ws_acc, B, ws.R, nsplit, nullptr, static_cast<__bf16*>(out), lse);
+  else if (crows >= kCombineFewRows)
+    hipLaunchKernelGGL((verify_combine_kernel<false, 4>), dim3((unsigned)crows), dim3(256), 0, stream, ws.ws_ml,
+                       ws.ws_acc, B, ws.R, nsplit, nullptr, static_cast<__bf16*>(out), lse);
+  else
+    hipLaunchKernelGGL((verify_combine_kernel<false, 16>), dim3((unsigned)crows), dim3(1024), 0, stream, ws.ws_ml,
+                       ws.ws_acc, B, ws.R, nsplit, nullptr, static_cast<__bf16*>(out), lse);
   return hipGetLastError() == hipSuccess ? MLA_VERIFY_OK : MLA_VERIFY_ERR_LAUNCH;
 }
 
@@ -1093,8 +1141,15 @@ int launch_balanced_partial(const void* q_nope, const void* q_rope, const void* 
 
 int launch_balanced_combine(const BalancedLaunch& ws, int B, int units, void* out, float* lse, hipStream_t stream) {
   const long long crows = (long long)B * ws.R;
-  hipLaunchKernelGGL(verify_combine_kernel<true>, dim3((unsigned)((crows + 3) / 4)), dim3(256), 0, stream, ws.ws_ml,
-                     ws.ws_acc, B, ws.R, units, (const int*)ws.split_start, static_cast<__bf16*>(out), lse);
+  if (crows >= kCombineManyRows)
+    hipLaunchKernelGGL((verify_combine_kernel<true, 1>), dim3((unsigned)((crows + 3) / 4)), dim3(256), 0, stream,
+                       ws.ws_ml, ws.ws_acc, B, ws.R, units, (const int*)ws.split_start, static_cast<__bf16*>(out), lse);
+  else if (crows >= kCombineFewRows)
+    hipLaunchKernelGGL((verify_combine_kernel<true, 4>), dim3((unsigned)crows), dim3(256), 0, stream, ws.ws_ml,
+                       ws.ws_acc, B, ws.R, units, (const int*)ws.split_start, static_cast<__bf16*>(out), lse);
+  else
+    hipLaunchKernelGGL((verify_combine_kernel<true, 16>), dim3((unsigned)crows), dim3(1024), 0, stream, ws.ws_ml,
+                       ws.ws_acc, B, ws.R, units, (const int*)ws.split_start, static_cast<__bf16*>(out), lse);
   return hipGetLastError() == hipSuccess ? MLA_VERIFY_OK : MLA_VERIFY_ERR_LAUNCH;
 }
 

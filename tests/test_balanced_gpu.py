@@ -130,3 +130,58 @@ def test_balanced_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(call.out.view(torch.int16), ref_out.view(torch.int16)), f"replay {k}"
         assert torch.equal(call.lse, ref_lse)
+
+
+@pytest.mark.parametrize("name,layout,units", [("4k_h64", None, 51), ("16k_h64", "contiguous", 51),
+                                               ("16k_h64", "scattered", 51), ("65k_h8", None, 256)])
+def test_balanced_configs_full(name, layout, units):
+    """The single-request workloads under the balanced schedule with one workgroup per CU (256 CUs /
+    row tiles), every output row against the oracle."""
+    wl = W.CONFIGS[name]
+    _say(f"[balanced] config {name} layout={layout or wl.layout} units={units}")
+    inp = W.make_inputs(wl, layout=layout)
+    call = DeviceCall(inp)
+    call.run(units, balanced=True)
+    got_out, got_lse = call.host()
+    ref_out, ref_lse = _oracle_full(inp)
+    compare(got_out, got_lse, ref_out, ref_lse, f"{name} balanced {units}")
+
+
+def test_balanced_relabel_and_onehot():
+    """Contiguous vs scattered placement of the same rows: bit-identical under the balanced schedule;
+    and the one-hot probe (q = 0, value row c = e_c) selects exactly the visible columns."""
+    inp = W.make_custom(np.random.default_rng(60), (300, 41), 9, 4)
+    pool, ki, oc = W.compact_inputs(inp)
+    a = DeviceCall(inp)
+    a.run(7, balanced=True)
+    out_a, lse_a = a.out.clone(), a.lse.clone()
+    b = DeviceCall(inp, pool=pool)
+    b.kv_indices = torch.from_numpy(ki).to(b.dev)
+    b.out_cache_loc = torch.from_numpy(oc).to(b.dev)
+    b.run(7, balanced=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a.view(torch.int16), b.out.view(torch.int16)) and torch.equal(lse_a, b.lse)
+
+    inp.q_nope[:] = 0
+    inp.q_rope[:] = 0
+    one = W.bf16_from_f32(np.ones(1, np.float32))[0]
+    pos = 0
+    for r in range(inp.B):
+        L = inp.prefixes[r] + inp.q_len
+        rows = inp.ref_rows[pos:pos + L]
+        rows[:] = 0
+        rows[np.arange(L), np.arange(L)] = one
+        pos += L
+    c = DeviceCall(inp)
+    c.run(7, balanced=True)
+    got = c.out.float().cpu().numpy()
+    for r in range(inp.B):
+        L = inp.prefixes[r] + inp.q_len
+        m = inp.custom_mask[inp.mask_indptr[r]:inp.mask_indptr[r] + inp.q_len * L].reshape(inp.q_len, L)
+        for i in range(inp.q_len):
+            n = int(m[i].sum())
+            expect = np.zeros(512)
+            expect[:L][m[i] != 0] = W.bf16_to_f32(W.bf16_from_f32(np.array([1.0 / n], np.float32)))[0]
+            for h in range(inp.H):
+                assert np.array_equal(np.flatnonzero(got[r, i, h]), np.flatnonzero(expect)), (r, i, h)
+                assert np.abs(got[r, i, h] - expect).max() <= 2 ** -8 / n
