@@ -165,10 +165,10 @@ int mla_verify_attn_combine(const void *workspace, size_t workspace_bytes, int B
  * MLA_VERIFY_ERR_NSPLIT. The result equals mla_verify_attn's up to rounding order; with units = B
  * every request gets one split and the result is bit-identical to mla_verify_attn with nsplit = 1.
  *
- * The workspace holds the plan (split_start int32 [B + 1]: the running sum of n_b; req_of_split
- * int32 [units]: the request of each split, -1 if unused), then float2 ml [units][q_len*H] and float
- * acc [units][q_len*H][512] partials (split split_start[b] + s of request b at block
- * split_start[b] + s), each region 256-byte aligned. mla_verify_attn_balanced_partial writes the plan
+ * The workspace holds the plan (split_info int32x4 [units]: {request, first column, end column, 0}
+ * of each split, {-1, 0, 0, 0} if unused; then split_start int32 [B + 1]: the running sum of n_b),
+ * then float2 ml [units][q_len*H] and float acc [units][q_len*H][512] partials (split
+ * split_start[b] + s of request b at block split_start[b] + s), each region 256-byte aligned. mla_verify_attn_balanced_partial writes the plan
  * (one-workgroup kernel) and the partials; mla_verify_attn_balanced_combine reads both.
  * mla_verify_attn_balanced_workspace_size returns 0 for arguments out of range.
  */

@@ -700,12 +700,13 @@ __device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds
       for (int eb = 0; eb < kHalfEBlocks; ++eb) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int e0 = 256 * hf + 32 * eb + 8 * j + 4 * g;
-          const uint2 v = *reinterpret_cast<const uint2*>(vrow + 2 * e0);
-          oacc[i][eb][4 * j + 0] += r * __uint_as_float(v.x << 16);
-          oacc[i][eb][4 * j + 1] += r * __uint_as_float(v.x & 0xFFFF0000u);
-          oacc[i][eb][4 * j + 2] += r * __uint_as_float(v.y << 16);
-          oacc[i][eb][4 * j + 3] += r * __uint_as_float(v.y & 0xFFFF0000u);
+          // one 16-byte load covers values 8j .. 8j+7 of the block; this lane's four are half g of it
+          const uint4 v = *reinterpret_cast<const uint4*>(vrow + 2 * (256 * hf + 32 * eb + 8 * j));
+          const uint32_t lo = g ? v.z : v.x, hi = g ? v.w : v.y;
+          oacc[i][eb][4 * j + 0] += r * __uint_as_float(lo << 16);
+          oacc[i][eb][4 * j + 1] += r * __uint_as_float(lo & 0xFFFF0000u);
+          oacc[i][eb][4 * j + 2] += r * __uint_as_float(hi << 16);
+          oacc[i][eb][4 * j + 3] += r * __uint_as_float(hi & 0xFFFF0000u);
         }
       }
     }
@@ -787,11 +788,13 @@ __device__ __forceinline__ long long wave_sum(long long x) {
   return x;
 }
 
-// split_start [B + 1] and req_of_split [units] (-1 for unused splits).
+// split_info [units] = {request, first column, end column, 0} ({-1, 0, 0, 0} for unused splits) and
+// split_start [B + 1]. A split's workgroups read their whole assignment with one load.
 __global__ void __launch_bounds__(kPlanThreads)
 verify_plan_kernel(const int32_t* __restrict__ kv_indptr, int B, int q_len, int units,
-                   int* __restrict__ split_start, int* __restrict__ req_of_split) {
+                   int* __restrict__ split_start, int4* __restrict__ split_info) {
   __shared__ int tiles[MLA_VERIFY_BALANCED_MAX_B];
+  __shared__ int lens[MLA_VERIFY_BALANCED_MAX_B];
   __shared__ int start_s[MLA_VERIFY_BALANCED_MAX_B + 1];
   const int lane = threadIdx.x;
   int tmax = 1;
@@ -799,6 +802,7 @@ verify_plan_kernel(const int32_t* __restrict__ kv_indptr, int B, int q_len, int 
     const long long L = max((long long)kv_indptr[b + 1] - (long long)kv_indptr[b], 0LL) + q_len;
     const int t = (int)((L + kTile - 1) / kTile);
     tiles[b] = t;
+    lens[b] = (int)L;
     tmax = max(tmax, t);
   }
   for (int d = 32; d >= 1; d >>= 1) tmax = max(tmax, __shfl_xor(tmax, d, 64));
@@ -833,7 +837,15 @@ verify_plan_kernel(const int32_t* __restrict__ kv_indptr, int B, int q_len, int 
       const int mid = (l + h) >> 1;
       if (start_s[mid] <= j) l = mid; else h = mid;
     }
-    req_of_split[j] = j < start_s[B] ? l : -1;
+    if (j < start_s[B]) {
+      const int s = j - start_s[l], n = start_s[l + 1] - start_s[l];
+      const long long T = tiles[l];
+      const int c0 = (int)((long long)s * T / n) * kTile;
+      const int c1 = min(lens[l], (int)((long long)(s + 1) * T / n) * kTile);
+      split_info[j] = make_int4(l, c0, c1, 0);
+    } else {
+      split_info[j] = make_int4(-1, 0, 0, 0);
+    }
   }
 }
 
@@ -846,8 +858,8 @@ verify_partial_balanced_kernel(const __bf16* __restrict__ q_nope, const __bf16* 
                                const int32_t* __restrict__ out_cache_loc,
                                const uint8_t* __restrict__ custom_mask,
                                const int32_t* __restrict__ mask_indptr, int B, int q_len, int H,
-                               float scale_log2, int units, int n_rt, const int* __restrict__ split_start,
-                               const int* __restrict__ req_of_split, float2* __restrict__ ws_ml,
+                               float scale_log2, int units, int n_rt, const int4* __restrict__ split_info,
+                               float2* __restrict__ ws_ml,
                                float* __restrict__ ws_acc) {
   PARTIAL_LDS_DECL
   const PartialArgs a = {q_nope, q_rope, kv_pool, N, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
@@ -855,24 +867,19 @@ verify_partial_balanced_kernel(const __bf16* __restrict__ q_nope, const __bf16* 
   const int xcd = (int)(blockIdx.x % 8), k = (int)(blockIdx.x / 8);
   const int j = xcd + 8 * (k / n_rt), rt = k % n_rt;
   if (j >= units) return;
-  const int b = req_of_split[j];
-  if (b < 0) return;
-  const int s0 = split_start[b];
-  const int n_b = split_start[b + 1] - s0, s = j - s0;
-  const int L = max(kv_indptr[b + 1] - kv_indptr[b], 0) + q_len;
-  const long long T_b = (L + kTile - 1) / kTile;
-  const int c_begin = (int)((long long)s * T_b / n_b) * kTile;
-  const int c_end = min(L, (int)((long long)(s + 1) * T_b / n_b) * kTile);
+  const int4 info = split_info[j];  // {request, first column, end column}
+  if (info.x < 0) return;
+  const int b = info.x, c_begin = info.y, c_end = info.z;
   run_split(a, lds, b, c_begin, c_end, rt, (size_t)j * (q_len * H));
 }
 
 // kWaves waves per query row (b, r): weights w_s = 2^(m_s - M) over the non-empty partials,
 // out = sum w_s acc_s / sum w_s l_s, lse = (M + log2 sum w_s l_s) * ln 2. Lane k owns output columns
-// [8k, 8k+8); wave w of a row takes splits w, w + kWaves, ..., 8 (4 with 16 waves) at a time with all
-// their loads issued together, and waves 1.. hand their sums to wave 0 through LDS. One wave per row (4 rows per
-// workgroup) suits many rows (the ragged 185k batch, 4096 rows); more waves per row keep the chip busy
-// when there are few rows and many splits (72 rows x 256 splits with one wave each left most CUs idle
-// and walked 256 splits serially: 95 us, against 26 us with four waves).
+// [8k, 8k+8); wave w of a row takes splits w, w + kWaves, ..., 8 (4 with 16 waves) at a time with
+// all their loads issued together, and waves 1.. hand their sums to wave 0 through LDS. One wave per
+// row (4 rows per workgroup) suits many rows (the ragged 185k batch, 4096 rows); more waves per row
+// keep the chip busy when there are few rows and many splits (72 rows x 256 splits with one wave each
+// left most CUs idle and walked 256 splits serially: 95 us, against 11 us with sixteen waves).
 // kBalanced: the partials of request b are blocks split_start[b] .. split_start[b+1] - 1 (the plan);
 // otherwise the nsplit blocks b * nsplit .. b * nsplit + nsplit - 1.
 template <int kWaves>
@@ -997,7 +1004,7 @@ bool sizes_ok(int B, int q_len, int H) {
   return rows <= (1LL << 24) && (long long)B * rows <= (1LL << 30);
 }
 
-// Balanced workspace: the plan (split_start int32 [B + 1], req_of_split int32 [units]), then (m, l)
+// Balanced workspace: the plan (split_info int32x4 [units], split_start int32 [B + 1]), then (m, l)
 // and accumulators for `units` partial row blocks, each region 256-byte aligned.
 struct BalancedLayout {
   size_t plan_bytes, ml_bytes, acc_bytes;
@@ -1005,7 +1012,7 @@ struct BalancedLayout {
 
 BalancedLayout balanced_layout(int B, int q_len, int H, int units) {
   const size_t rows = (size_t)units * q_len * H;
-  return {align_up((size_t)(B + 1 + units) * sizeof(int), MLA_VERIFY_WORKSPACE_ALIGN),
+  return {align_up((size_t)units * sizeof(int4) + (size_t)(B + 1) * sizeof(int), MLA_VERIFY_WORKSPACE_ALIGN),
           align_up(rows * sizeof(float2), MLA_VERIFY_WORKSPACE_ALIGN),
           align_up(rows * kLatent * sizeof(float), MLA_VERIFY_WORKSPACE_ALIGN)};
 }
@@ -1097,7 +1104,7 @@ int launch_combine(const Launch& ws, int B, int nsplit, void* out, float* lse, h
 
 struct BalancedLaunch {
   int* split_start;
-  int* req_of_split;
+  int4* split_info;
   float2* ws_ml;
   float* ws_acc;
   int R;
@@ -1116,7 +1123,7 @@ int check_balanced(int B, int q_len, int H, int units, const void* workspace, si
 BalancedLaunch balanced_workspace(void* workspace, int B, int q_len, int H, int units) {
   const BalancedLayout lay = balanced_layout(B, q_len, H, units);
   uint8_t* w = static_cast<uint8_t*>(workspace);
-  return {reinterpret_cast<int*>(w), reinterpret_cast<int*>(w) + (B + 1),
+  return {reinterpret_cast<int*>(w + (size_t)units * sizeof(int4)), reinterpret_cast<int4*>(w),
           reinterpret_cast<float2*>(w + lay.plan_bytes), reinterpret_cast<float*>(w + lay.plan_bytes + lay.ml_bytes),
           q_len * H};
 }
@@ -1129,13 +1136,13 @@ int launch_balanced_partial(const void* q_nope, const void* q_rope, const void* 
   const long long grid = ((long long)units + 7) / 8 * 8 * n_rt;
   if (grid > INT32_MAX) return MLA_VERIFY_ERR_SHAPE;
   hipLaunchKernelGGL(verify_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, kv_indptr, B, q_len, units,
-                     ws.split_start, ws.req_of_split);
+                     ws.split_start, ws.split_info);
   if (hipGetLastError() != hipSuccess) return MLA_VERIFY_ERR_LAUNCH;
   hipLaunchKernelGGL(verify_partial_balanced_kernel, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream,
                      static_cast<const __bf16*>(q_nope), static_cast<const __bf16*>(q_rope),
                      static_cast<const uint8_t*>(kv_pool), (int)N, kv_indptr, kv_indices, out_cache_loc, custom_mask,
                      mask_indptr, B, q_len, H, scale * 1.44269504088896340736f, units, n_rt,
-                     (const int*)ws.split_start, (const int*)ws.req_of_split, ws.ws_ml, ws.ws_acc);
+                     (const int4*)ws.split_info, ws.ws_ml, ws.ws_acc);
   return hipGetLastError() == hipSuccess ? MLA_VERIFY_OK : MLA_VERIFY_ERR_LAUNCH;
 }
 

@@ -119,7 +119,7 @@ def test_kv_compact_validates_before_any_hip_call():
 
 def test_balanced_workspace_size_and_validation():
     rows = 40 * 16 * 64
-    plan = -(-(5 + 40) * 4 // 256) * 256
+    plan = -(-(40 * 16 + 5 * 4) // 256) * 256
     expect = plan + -(-rows * 8 // 256) * 256 + -(-rows * 2048 // 256) * 256
     assert pkg.balanced_workspace_size(4, 16, 64, 40) == expect
     assert pkg.balanced_workspace_size(4, 16, 64, 3) == 0          # fewer units than requests

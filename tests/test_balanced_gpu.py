@@ -85,10 +85,13 @@ def test_plan_bit_exact(prefixes, q_len, units):
                                   0.07, units, ws.data_ptr(), ws.numel(), None)
     assert rc == 0
     torch.cuda.synchronize()
-    plan = ws[: 4 * (B + 1 + units)].cpu().numpy().view(np.int32)
-    split_start, req, _ = S.balanced_plan(ip, B, q_len, units)
-    assert plan[:B + 1].tolist() == split_start
-    assert plan[B + 1:].tolist() == req
+    plan = ws[: 16 * units + 4 * (B + 1)].cpu().numpy().view(np.int32)
+    split_start, req, ranges = S.balanced_plan(ip, B, q_len, units)
+    info = plan[:4 * units].reshape(units, 4)
+    expect = [[b, c0, c1, 0] for b, c0, c1 in ranges] + [[-1, 0, 0, 0]] * (units - len(ranges))
+    assert info.tolist() == expect
+    assert info[:, 0].tolist() == req
+    assert plan[4 * units:].tolist() == split_start
 
 
 @pytest.mark.parametrize("units", [32, 64])
