@@ -77,6 +77,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -694,6 +695,8 @@ __device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds
   for (int i = 0; i < 2; ++i) {
     const float r = i == 0 ? r_own : r_par;
     const int c = i == 0 ? col_own : col_par;
+    // both lanes of a pair hold the same row, hence the same r and column: the pair is active or
+    // inactive as a whole, and the swaps below only read active partners
     if (set_row(i) < R && r != 0.0f) {
       int slot = c < P ? kv_indices[kv_start + c] : out_cache_loc[(size_t)b * q_len + (c - P)];
       slot = min(max(slot, 0), a.N - 1);
@@ -701,14 +704,26 @@ __device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds
 #pragma unroll
       for (int eb = 0; eb < kHalfEBlocks; ++eb) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // one 16-byte load covers values 8j .. 8j+7 of the block; this lane's four are half g of it
-          const uint4 v = *reinterpret_cast<const uint4*>(vrow + 2 * (256 * hf + 32 * eb + 8 * j));
-          const uint32_t lo = g ? v.z : v.x, hi = g ? v.w : v.y;
-          oacc[i][eb][4 * j + 0] += r * __uint_as_float(lo << 16);
-          oacc[i][eb][4 * j + 1] += r * __uint_as_float(lo & 0xFFFF0000u);
-          oacc[i][eb][4 * j + 2] += r * __uint_as_float(hi << 16);
-          oacc[i][eb][4 * j + 3] += r * __uint_as_float(hi & 0xFFFF0000u);
+        for (int jj = 0; jj < 2; ++jj) {
+          // values 8j .. 8j+7 of the block (j = 2jj, 2jj+1) sit in one 16-byte chunk each, and a lane
+          // needs half g of both: lane g loads chunk 2jj+g, keeps its own half and swaps the other
+          // half with its partner
+          const u32x4 v = *reinterpret_cast<const u32x4*>(vrow + 2 * (256 * hf + 32 * eb + 8 * (2 * jj + g)));
+          const uint32_t send0 = g ? v[0] : v[2], send1 = g ? v[1] : v[3];
+          const auto x0 = __builtin_amdgcn_permlane32_swap(send0, send0, false, false);
+          const auto x1 = __builtin_amdgcn_permlane32_swap(send1, send1, false, false);
+          // after a swap of (u, u) the partner's u is result 1 in the low half and result 0 in the high
+          const uint32_t recv0 = g ? x0[0] : x0[1], recv1 = g ? x1[0] : x1[1];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int j = 2 * jj + h;
+            const bool mine = h == g;  // chunk j is the one this lane loaded
+            const uint32_t lo = mine ? v[2 * g] : recv0, hi = mine ? v[2 * g + 1] : recv1;
+            oacc[i][eb][4 * j + 0] += r * __uint_as_float(lo << 16);
+            oacc[i][eb][4 * j + 1] += r * __uint_as_float(lo & 0xFFFF0000u);
+            oacc[i][eb][4 * j + 2] += r * __uint_as_float(hi << 16);
+            oacc[i][eb][4 * j + 3] += r * __uint_as_float(hi & 0xFFFF0000u);
+          }
         }
       }
     }
