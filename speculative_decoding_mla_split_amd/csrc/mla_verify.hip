@@ -64,6 +64,7 @@ constexpr int kMetaExtra = 2;                    // extra mask loads at most (bl
 constexpr int kMetaTokens = 1 + 2 * kMetaExtra;  // block tokens whose mask bytes ride in LDS
 constexpr int kMetaBytes = 256 * (1 + kMetaExtra);
 constexpr int kMetaStages = 8;                   // per-wave ring of per-tile metadata
+constexpr int kCorrBatch = 2;  // value blocks whose loads the top-probability correction issues together
 constexpr int kLdsBytes = kBufs * kTileBytes + kWaves * (kSXchgBytes + kPXchgBytes + kMetaStages * kMetaBytes);
 
 static_assert(kRowsPerLoader * kChunks % 64 == 0, "loader must tile whole wave instructions");
@@ -691,38 +692,49 @@ __device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds
   lds_barrier();
   const float r_par = xch[((w ^ 1) * 32 + (lane & 31)) * 2];
   const int col_par = __float_as_int(xch[((w ^ 1) * 32 + (lane & 31)) * 2 + 1]);
+  // Both lanes of a pair hold the same row, hence the same r and column: a pair is active or
+  // inactive as a whole, and the swaps below only read active partners. Values 8j .. 8j+7 of an
+  // output block (j = 2jj, 2jj+1) sit in one 16-byte chunk each and a lane needs half g of both:
+  // lane g loads chunk 2jj+g, keeps its own half and swaps the other half with its partner. The
+  // loads of kCorrBatch blocks go out together ahead of their first use (left to itself the compiler
+  // waits for each load before issuing the next, paying the memory latency 16 times per set).
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const float r = i == 0 ? r_own : r_par;
     const int c = i == 0 ? col_own : col_par;
-    // both lanes of a pair hold the same row, hence the same r and column: the pair is active or
-    // inactive as a whole, and the swaps below only read active partners
     if (set_row(i) < R && r != 0.0f) {
       int slot = c < P ? kv_indices[kv_start + c] : out_cache_loc[(size_t)b * q_len + (c - P)];
       slot = min(max(slot, 0), a.N - 1);
-      const uint8_t* vrow = kv_pool + (size_t)slot * kRowBytes;
+      const uint8_t* vrow = kv_pool + (size_t)slot * kRowBytes + 2 * (256 * hf + 8 * g);
 #pragma unroll
-      for (int eb = 0; eb < kHalfEBlocks; ++eb) {
+      for (int e0 = 0; e0 < kHalfEBlocks; e0 += kCorrBatch) {
+        u32x4 vv[kCorrBatch][2];
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          // values 8j .. 8j+7 of the block (j = 2jj, 2jj+1) sit in one 16-byte chunk each, and a lane
-          // needs half g of both: lane g loads chunk 2jj+g, keeps its own half and swaps the other
-          // half with its partner
-          const u32x4 v = *reinterpret_cast<const u32x4*>(vrow + 2 * (256 * hf + 32 * eb + 8 * (2 * jj + g)));
-          const uint32_t send0 = g ? v[0] : v[2], send1 = g ? v[1] : v[3];
-          const auto x0 = __builtin_amdgcn_permlane32_swap(send0, send0, false, false);
-          const auto x1 = __builtin_amdgcn_permlane32_swap(send1, send1, false, false);
-          // after a swap of (u, u) the partner's u is result 1 in the low half and result 0 in the high
-          const uint32_t recv0 = g ? x0[0] : x0[1], recv1 = g ? x1[0] : x1[1];
+        for (int e = 0; e < kCorrBatch; ++e)
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int j = 2 * jj + h;
-            const bool mine = h == g;  // chunk j is the one this lane loaded
-            const uint32_t lo = mine ? v[2 * g] : recv0, hi = mine ? v[2 * g + 1] : recv1;
-            oacc[i][eb][4 * j + 0] += r * __uint_as_float(lo << 16);
-            oacc[i][eb][4 * j + 1] += r * __uint_as_float(lo & 0xFFFF0000u);
-            oacc[i][eb][4 * j + 2] += r * __uint_as_float(hi << 16);
-            oacc[i][eb][4 * j + 3] += r * __uint_as_float(hi & 0xFFFF0000u);
+          for (int jj = 0; jj < 2; ++jj)
+            vv[e][jj] = *reinterpret_cast<const u32x4*>(vrow + 2 * (32 * (e0 + e) + 16 * jj));
+#pragma unroll
+        for (int e = 0; e < kCorrBatch; ++e) {
+          const int eb = e0 + e;
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const u32x4 v = vv[e][jj];
+            const uint32_t send0 = g ? v[0] : v[2], send1 = g ? v[1] : v[3];
+            const auto x0 = __builtin_amdgcn_permlane32_swap(send0, send0, false, false);
+            const auto x1 = __builtin_amdgcn_permlane32_swap(send1, send1, false, false);
+            // after a swap of (u, u) the partner's u is result 1 in the low half and result 0 in the high
+            const uint32_t recv0 = g ? x0[0] : x0[1], recv1 = g ? x1[0] : x1[1];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int j = 2 * jj + h;
+              const bool mine = h == g;  // chunk j is the one this lane loaded
+              const uint32_t lo = mine ? v[2 * g] : recv0, hi = mine ? v[2 * g + 1] : recv1;
+              oacc[i][eb][4 * j + 0] += r * __uint_as_float(lo << 16);
+              oacc[i][eb][4 * j + 1] += r * __uint_as_float(lo & 0xFFFF0000u);
+              oacc[i][eb][4 * j + 2] += r * __uint_as_float(hi << 16);
+              oacc[i][eb][4 * j + 3] += r * __uint_as_float(hi & 0xFFFF0000u);
+            }
           }
         }
       }
