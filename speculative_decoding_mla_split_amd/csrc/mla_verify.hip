@@ -109,12 +109,6 @@ __host__ __device__ constexpr int tile_offset(int c, int k) {
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)reinterpret_cast<uintptr_t>((lds_void*)p));
 }
-__device__ __forceinline__ void dma_b128(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
-}
-__device__ __forceinline__ void dma_b32(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
-}
 // Group j of a loader wave's region: global src + 128j -> LDS lds + 1024j (+ 16 * lane). The
 // immediate offset is added to both addresses, so m0 is set to lds + 896j.
 template <int J>
@@ -878,8 +872,55 @@ verify_plan_kernel(const int32_t* __restrict__ kv_indptr, int B, int q_len, int 
   }
 }
 
+// The same plan for batches of at most 64 requests, computed by one wave inside the partial kernel
+// (lane b holds request b) for split j alone: {request, first column, end column, 0}, or
+// {-1, 0, 0, 0} when the plan leaves split j unused. Every wave of every workgroup computes it (a
+// dozen search steps of wave reductions, cheaper than a separate launch in front of the kernel),
+// with the integer arithmetic of verify_plan_kernel, so the two give identical plans. Lanes b < B
+// return their request's running split count in *start_excl and *start_incl.
+constexpr int kFusedPlanMaxB = 64;
+__device__ __forceinline__ int4 plan_split_wave(const int32_t* __restrict__ kv_indptr, int B, int q_len, int units,
+                                                int j, int lane, int* start_excl, int* start_incl) {
+  int T = 0, Lb = 0;
+  if (lane < B) {
+    const long long L = max((long long)kv_indptr[lane + 1] - (long long)kv_indptr[lane], 0LL) + q_len;
+    T = (int)((L + kTile - 1) / kTile);
+    Lb = (int)L;
+  }
+  int tmax = max(T, 1);
+  for (int d = 32; d >= 1; d >>= 1) tmax = max(tmax, __shfl_xor(tmax, d, 64));
+  unsigned lo = 1, hi = (unsigned)tmax;
+  while (lo < hi) {
+    const unsigned mid = (lo + hi) / 2;
+    const long long cnt = lane < B ? (long long)(((unsigned)T + mid - 1) / mid) : 0;
+    if (wave_sum(cnt) <= units) hi = mid; else lo = mid + 1;
+  }
+  const unsigned C = lo;
+  const int n = lane < B ? (int)(((unsigned)T + C - 1) / C) : 0;
+  int incl = n;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
+  }
+  const int excl = incl - n;
+  *start_excl = excl;
+  *start_incl = incl;
+  const unsigned long long own = __ballot(lane < B && excl <= j && j < incl);
+  if (own == 0) return make_int4(-1, 0, 0, 0);
+  const int l = __ffsll((long long)own) - 1;
+  const int s_l = j - __shfl(excl, l, 64), n_l = __shfl(n, l, 64);
+  const long long T_l = __shfl(T, l, 64);
+  const int L_l = __shfl(Lb, l, 64);
+  const int c0 = (int)((long long)s_l * T_l / n_l) * kTile;
+  const int c1 = min(L_l, (int)((long long)(s_l + 1) * T_l / n_l) * kTile);
+  return make_int4(l, c0, c1, 0);
+}
+
 // Workgroup -> (split j, row tile): split j on XCD j % 8 with all its row tiles (they read the same KV
-// rows). The grid is 8 * ceil(units / 8) * n_rt; splits the plan leaves unused exit at once.
+// rows). The grid is 8 * ceil(units / 8) * n_rt; splits the plan leaves unused exit at once. With
+// fused_plan (B <= kFusedPlanMaxB) the workgroups compute their split themselves and write the plan
+// records (split_info[j] by split j's first row tile, split_start by workgroup 0); otherwise they
+// read split_info, which verify_plan_kernel wrote.
 __global__ void __launch_bounds__(kWaves * 64, 1)
 verify_partial_balanced_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restrict__ q_rope,
                                const uint8_t* __restrict__ kv_pool, int N,
@@ -887,8 +928,8 @@ verify_partial_balanced_kernel(const __bf16* __restrict__ q_nope, const __bf16* 
                                const int32_t* __restrict__ out_cache_loc,
                                const uint8_t* __restrict__ custom_mask,
                                const int32_t* __restrict__ mask_indptr, int B, int q_len, int H,
-                               float scale_log2, int units, int n_rt, const int4* __restrict__ split_info,
-                               float2* __restrict__ ws_ml,
+                               float scale_log2, int units, int n_rt, int fused_plan, int4* __restrict__ split_info,
+                               int* __restrict__ split_start, float2* __restrict__ ws_ml,
                                float* __restrict__ ws_acc) {
   PARTIAL_LDS_DECL
   const PartialArgs a = {q_nope, q_rope, kv_pool, N, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
@@ -896,7 +937,22 @@ verify_partial_balanced_kernel(const __bf16* __restrict__ q_nope, const __bf16* 
   const int xcd = (int)(blockIdx.x % 8), k = (int)(blockIdx.x / 8);
   const int j = xcd + 8 * (k / n_rt), rt = k % n_rt;
   if (j >= units) return;
-  const int4 info = split_info[j];  // {request, first column, end column}
+  int4 info;  // {request, first column, end column}
+  if (fused_plan) {
+    const int lane = threadIdx.x & 63;
+    int excl, incl;
+    info = plan_split_wave(kv_indptr, B, q_len, units, j, lane, &excl, &incl);
+    if (threadIdx.x < 64) {
+      if (rt == 0 && lane == 0) split_info[j] = info;
+      if (blockIdx.x == 0) {
+        if (lane == 0) split_start[0] = 0;
+        if (lane < B) split_start[lane + 1] = incl;
+      }
+    }
+    info = make_int4(wave_uniform(info.x), wave_uniform(info.y), wave_uniform(info.z), 0);
+  } else {
+    info = split_info[j];
+  }
   if (info.x < 0) return;
   const int b = info.x, c_begin = info.y, c_end = info.z;
   run_split(a, lds, b, c_begin, c_end, rt, (size_t)j * (q_len * H));
@@ -1164,14 +1220,17 @@ int launch_balanced_partial(const void* q_nope, const void* q_rope, const void* 
   const int n_rt = (ws.R + kRowsPerWG - 1) / kRowsPerWG;
   const long long grid = ((long long)units + 7) / 8 * 8 * n_rt;
   if (grid > INT32_MAX) return MLA_VERIFY_ERR_SHAPE;
-  hipLaunchKernelGGL(verify_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, kv_indptr, B, q_len, units,
-                     ws.split_start, ws.split_info);
-  if (hipGetLastError() != hipSuccess) return MLA_VERIFY_ERR_LAUNCH;
+  const int fused = B <= kFusedPlanMaxB ? 1 : 0;
+  if (!fused) {
+    hipLaunchKernelGGL(verify_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, kv_indptr, B, q_len, units,
+                       ws.split_start, ws.split_info);
+    if (hipGetLastError() != hipSuccess) return MLA_VERIFY_ERR_LAUNCH;
+  }
   hipLaunchKernelGGL(verify_partial_balanced_kernel, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream,
                      static_cast<const __bf16*>(q_nope), static_cast<const __bf16*>(q_rope),
                      static_cast<const uint8_t*>(kv_pool), (int)N, kv_indptr, kv_indices, out_cache_loc, custom_mask,
-                     mask_indptr, B, q_len, H, scale * 1.44269504088896340736f, units, n_rt,
-                     (const int4*)ws.split_info, ws.ws_ml, ws.ws_acc);
+                     mask_indptr, B, q_len, H, scale * 1.44269504088896340736f, units, n_rt, fused,
+                     (int4*)ws.split_info, (int*)ws.split_start, ws.ws_ml, ws.ws_acc);
   return hipGetLastError() == hipSuccess ? MLA_VERIFY_OK : MLA_VERIFY_ERR_LAUNCH;
 }
 

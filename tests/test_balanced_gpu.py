@@ -58,10 +58,22 @@ def test_one_split_per_request_matches_nsplit_1_bit_exact(seed, prefixes, q_len,
     assert torch.equal(a_lse, call.lse)
 
 
+# Batches of up to 64 requests get their plan from the partial kernel's own workgroups, larger ones
+# from the separate one-wave plan kernel; both must write the oracle plan.
+_MANY_64 = tuple((37 * i) % 500 for i in range(64))
+_MANY_65 = tuple((53 * i + 11) % 700 for i in range(65))
+_MANY_300 = tuple((29 * i + 3) % 2000 for i in range(300))
+
+
 @pytest.mark.parametrize("prefixes,q_len,units", [((4096, 32768, 120000, 185000), 16, 32),
                                                   ((4096, 32768, 120000, 185000), 16, 100),
                                                   ((5, 0, 700, 64, 2500, 1), 9, 6),
-                                                  ((5, 0, 700, 64, 2500, 1), 9, 4096)])
+                                                  ((5, 0, 700, 64, 2500, 1), 9, 4096),
+                                                  (_MANY_64, 4, 64),
+                                                  (_MANY_64, 4, 333),
+                                                  (_MANY_65, 4, 65),
+                                                  (_MANY_65, 4, 200),
+                                                  (_MANY_300, 2, 1000)])
 def test_plan_bit_exact(prefixes, q_len, units):
     """The plan the device writes into the workspace equals the oracle plan (index work: exact)."""
     B = len(prefixes)
@@ -92,6 +104,18 @@ def test_plan_bit_exact(prefixes, q_len, units):
     assert info.tolist() == expect
     assert info[:, 0].tolist() == req
     assert plan[4 * units:].tolist() == split_start
+
+
+@pytest.mark.parametrize("prefixes,units", [(_MANY_64[:40], 97), (_MANY_65, 130)])
+def test_balanced_parity_many_requests(prefixes, units):
+    """40 requests (plan inside the partial kernel) and 65 requests (separate plan kernel)."""
+    _say(f"[balanced] B={len(prefixes)} units={units}")
+    inp = W.make_custom(np.random.default_rng(77), prefixes, 3, 2)
+    call = DeviceCall(inp)
+    call.run(units, balanced=True)
+    got_out, got_lse = call.host()
+    ref_out, ref_lse = _oracle_full(inp)
+    compare(got_out, got_lse, ref_out, ref_lse, f"balanced B={len(prefixes)} units {units}")
 
 
 @pytest.mark.parametrize("units", [32, 64])
