@@ -168,8 +168,10 @@ int mla_verify_attn_combine(const void *workspace, size_t workspace_bytes, int B
  * The workspace holds the plan (split_info int32x4 [units]: {request, first column, end column, 0}
  * of each split, {-1, 0, 0, 0} if unused; then split_start int32 [B + 1]: the running sum of n_b),
  * then float2 ml [units][q_len*H] and float acc [units][q_len*H][512] partials (split
- * split_start[b] + s of request b at block split_start[b] + s), each region 256-byte aligned. mla_verify_attn_balanced_partial writes the plan
- * (one-workgroup kernel) and the partials; mla_verify_attn_balanced_combine reads both.
+ * split_start[b] + s of request b at block split_start[b] + s), each region 256-byte aligned.
+ * mla_verify_attn_balanced_partial writes the plan and the partials (for B <= 64 the partial
+ * kernel's workgroups compute the plan themselves; larger batches get it from a one-wave kernel
+ * launched first, with the same result); mla_verify_attn_balanced_combine reads both.
  * mla_verify_attn_balanced_workspace_size returns 0 for arguments out of range.
  */
 size_t mla_verify_attn_balanced_workspace_size(int B, int q_len, int H, int units);
