@@ -65,7 +65,8 @@ typedef enum {
  * Bytes of workspace mla_verify_attn needs for these sizes ("From Capture Safety to MoE
  * Ceiling", "The Architecture of Capture Safety": the workspace is allocated once, outside
  * the step). It holds one partial per (request, split, draft token, head): the running max
- * and sum (2 floats) and the unnormalised 512-wide accumulator (512 floats).
+ * and sum (2 floats), the unnormalised 512-wide accumulator (512 floats) and the top record
+ * (16 bytes).
  * Returns 0 when an argument is out of range (B, q_len, H < 1; nsplit outside [1, 1024]).
  */
 size_t mla_verify_attn_workspace_size(int B, int q_len, int H, int nsplit);
@@ -127,11 +128,19 @@ int mla_verify_attn(const void *q_nope, const void *q_rope, const void *kv_pool,
  * mla_verify_attn_combine runs the reduction kernel of the same section on those partials and
  * writes out and lse. Between the two calls the workspace holds, for every (b, s, i, h), the
  * split's running max m (base-2 units of the scaled score, -inf for an empty or fully masked
- * split), its sum l of 2^(score*log2(e) - m) and its unnormalised 512-wide accumulator, laid out
- * as float2 ml[B][nsplit][q_len*H] followed (at the next 256-byte boundary) by
- * float acc[B][nsplit][q_len*H][512]. A caller may move these partials between the two calls
- * (for example to combine partials computed for different column ranges elsewhere); the combine
- * needs only this layout. Calls with the same (B, q_len, H, nsplit) must be used for both.
+ * split), its sum l of 2^(score*log2(e) - m), its unnormalised 512-wide accumulator (every
+ * probability rounded to bf16 before it multiplies a value row, as the matrix cores take it) and
+ * its top record: the exact probability p of the split's largest visible score (same base as l)
+ * and the device address of that column's 576-wide pool row. Laid out as
+ * float2 ml[B][nsplit][q_len*H], then float acc[B][nsplit][q_len*H][512], then
+ * int32x4 top[B][nsplit][q_len*H] = {bits of p, address low 32 bits, address high 32 bits, 0},
+ * each region starting at a 256-byte boundary. The combine adds w_s (p - bf16(p)) times the first
+ * 512 values of that row for every split whose p w_s is at least 1/32 of the row's final sum
+ * (exact probability restored for the columns that dominate a row); it reads the pool rows
+ * through the recorded addresses, so the pool must still be valid when it runs. A caller may
+ * move these partials between the two calls (for example to combine partials computed for
+ * different column ranges elsewhere); the combine needs only this layout. Calls with the same
+ * (B, q_len, H, nsplit) must be used for both.
  */
 int mla_verify_attn_partial(const void *q_nope, const void *q_rope, const void *kv_pool, int64_t N,
                             const int32_t *kv_indptr, const int32_t *kv_indices,
@@ -167,8 +176,9 @@ int mla_verify_attn_combine(const void *workspace, size_t workspace_bytes, int B
  *
  * The workspace holds the plan (split_info int32x4 [units]: {request, first column, end column, 0}
  * of each split, {-1, 0, 0, 0} if unused; then split_start int32 [B + 1]: the running sum of n_b),
- * then float2 ml [units][q_len*H] and float acc [units][q_len*H][512] partials (split
- * split_start[b] + s of request b at block split_start[b] + s), each region 256-byte aligned.
+ * then float2 ml [units][q_len*H], float acc [units][q_len*H][512] and int32x4 top
+ * [units][q_len*H] partials as described for mla_verify_attn_partial (split split_start[b] + s of
+ * request b at block split_start[b] + s), each region 256-byte aligned.
  * mla_verify_attn_balanced_partial writes the plan and the partials (for B <= 64 the partial
  * kernel's workgroups compute the plan themselves; larger batches get it from a one-wave kernel
  * launched first, with the same result); mla_verify_attn_balanced_combine reads both.

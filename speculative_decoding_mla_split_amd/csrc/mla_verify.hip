@@ -64,7 +64,6 @@ constexpr int kMetaExtra = 2;                    // extra mask loads at most (bl
 constexpr int kMetaTokens = 1 + 2 * kMetaExtra;  // block tokens whose mask bytes ride in LDS
 constexpr int kMetaBytes = 256 * (1 + kMetaExtra);
 constexpr int kMetaStages = 8;                   // per-wave ring of per-tile metadata
-constexpr int kCorrBatch = 2;  // value blocks whose loads the top-probability correction issues together
 constexpr int kLdsBytes = kBufs * kTileBytes + kWaves * (kSXchgBytes + kPXchgBytes + kMetaStages * kMetaBytes);
 
 static_assert(kRowsPerLoader * kChunks % 64 == 0, "loader must tile whole wave instructions");
@@ -504,6 +503,7 @@ struct PartialArgs {
   float scale_log2;
   float2* ws_ml;
   float* ws_acc;
+  int4* ws_top;
 };
 
 // The partial kernels' LDS.
@@ -653,15 +653,13 @@ __device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds
     m_ref = pair_max(best_raw) * x.scale_log2;  // the row's true max over the split
   }
 
-  // ---- exact top probability. Each visible column entered the PV product with its probability
-  // rounded to bf16 (the sum l took the exact values); for the row's largest one (the same fma +
-  // exp2 as in the tile, so the same value) add back what the rounding dropped, r = p - bf16(p),
-  // times its value row. Without this, a row dominated by one column whose score came after the
-  // reference tile is off by up to 2^-9 of that column's values. The lane pair first agrees on the
-  // row's best column; the pair's two waves then swap their own rows' (r, column) so each can
-  // correct its output half of both blocks.
-  float r_own;
-  int col_own;
+  // ---- the row's top probability. Each visible column entered the PV product with its probability
+  // rounded to bf16 (the sum l took the exact values). For the row's largest one (the same fma +
+  // exp2 as in the tile, so the same value) the exact probability and the address of its value row
+  // go to the top record; the combine adds back what the rounding dropped, (p - bf16(p)) times that
+  // value row, where the column matters against the row's final sum. Without that, a row dominated
+  // by one column whose score came after the reference tile is off by up to 2^-9 of that column's
+  // values. The lane pair first agrees on the row's best column.
   {
     const auto rs = __builtin_amdgcn_permlane32_swap(__float_as_uint(best_raw), __float_as_uint(best_raw), false,
                                                      false);
@@ -670,68 +668,15 @@ __device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds
     const int ca = (int)cs[0], cb = (int)cs[1];
     const bool take_b = rb > ra || (rb == ra && cb < ca);
     const float top = take_b ? rb : ra;
-    col_own = take_b ? cb : ca;
-    const float base = m_ref == -INFINITY ? 0.0f : m_ref;
-    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(top, x.scale_log2, -base));
-    // a top probability under 1/32 of the row's sum moves the output by at most 2^-14 of a value
-    // row if left rounded: skip its correction (and the value-row reads)
-    const float l_pair = pair_sum(l_lane);
-    r_own = top == -INFINITY || 32.0f * p < l_pair ? 0.0f : p - (float)(__bf16)p;
-  }
-  float* const xch = reinterpret_cast<float*>(lds.s);
-  if (lane < 32) {
-    xch[(w * 32 + lane) * 2] = r_own;
-    xch[(w * 32 + lane) * 2 + 1] = __int_as_float(col_own);
-  }
-  lds_barrier();
-  const float r_par = xch[((w ^ 1) * 32 + (lane & 31)) * 2];
-  const int col_par = __float_as_int(xch[((w ^ 1) * 32 + (lane & 31)) * 2 + 1]);
-  // Both lanes of a pair hold the same row, hence the same r and column: a pair is active or
-  // inactive as a whole, and the swaps below only read active partners. Values 8j .. 8j+7 of an
-  // output block (j = 2jj, 2jj+1) sit in one 16-byte chunk each and a lane needs half g of both:
-  // lane g loads chunk 2jj+g, keeps its own half and swaps the other half with its partner. The
-  // loads of kCorrBatch blocks go out together ahead of their first use (left to itself the compiler
-  // waits for each load before issuing the next, paying the memory latency 16 times per set).
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const float r = i == 0 ? r_own : r_par;
-    const int c = i == 0 ? col_own : col_par;
-    if (set_row(i) < R && r != 0.0f) {
-      int slot = c < P ? kv_indices[kv_start + c] : out_cache_loc[(size_t)b * q_len + (c - P)];
+    const int col = take_b ? cb : ca;
+    if (own_row < R && g == 0) {
+      const float base = m_ref == -INFINITY ? 0.0f : m_ref;
+      const float p = top == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(__builtin_fmaf(top, x.scale_log2, -base));
+      int slot = col < P ? kv_indices[kv_start + col] : out_cache_loc[(size_t)b * q_len + (col - P)];
       slot = min(max(slot, 0), a.N - 1);
-      const uint8_t* vrow = kv_pool + (size_t)slot * kRowBytes + 2 * (256 * hf + 8 * g);
-#pragma unroll
-      for (int e0 = 0; e0 < kHalfEBlocks; e0 += kCorrBatch) {
-        u32x4 vv[kCorrBatch][2];
-#pragma unroll
-        for (int e = 0; e < kCorrBatch; ++e)
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj)
-            vv[e][jj] = *reinterpret_cast<const u32x4*>(vrow + 2 * (32 * (e0 + e) + 16 * jj));
-#pragma unroll
-        for (int e = 0; e < kCorrBatch; ++e) {
-          const int eb = e0 + e;
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            const u32x4 v = vv[e][jj];
-            const uint32_t send0 = g ? v[0] : v[2], send1 = g ? v[1] : v[3];
-            const auto x0 = __builtin_amdgcn_permlane32_swap(send0, send0, false, false);
-            const auto x1 = __builtin_amdgcn_permlane32_swap(send1, send1, false, false);
-            // after a swap of (u, u) the partner's u is result 1 in the low half and result 0 in the high
-            const uint32_t recv0 = g ? x0[0] : x0[1], recv1 = g ? x1[0] : x1[1];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const int j = 2 * jj + h;
-              const bool mine = h == g;  // chunk j is the one this lane loaded
-              const uint32_t lo = mine ? v[2 * g] : recv0, hi = mine ? v[2 * g + 1] : recv1;
-              oacc[i][eb][4 * j + 0] += r * __uint_as_float(lo << 16);
-              oacc[i][eb][4 * j + 1] += r * __uint_as_float(lo & 0xFFFF0000u);
-              oacc[i][eb][4 * j + 2] += r * __uint_as_float(hi << 16);
-              oacc[i][eb][4 * j + 3] += r * __uint_as_float(hi & 0xFFFF0000u);
-            }
-          }
-        }
-      }
+      const uint64_t vrow = reinterpret_cast<uint64_t>(kv_pool + (size_t)slot * kRowBytes);
+      a.ws_top[part + own_row] =
+          make_int4(__float_as_int(p), (int)(uint32_t)vrow, (int)(uint32_t)(vrow >> 32), 0);
     }
   }
 
@@ -775,10 +720,10 @@ verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restric
                       const uint8_t* __restrict__ custom_mask,
                       const int32_t* __restrict__ mask_indptr, int B, int q_len, int H,
                       float scale_log2, int nsplit, int n_rt, float2* __restrict__ ws_ml,
-                      float* __restrict__ ws_acc) {
+                      float* __restrict__ ws_acc, int4* __restrict__ ws_top) {
   PARTIAL_LDS_DECL
   const PartialArgs a = {q_nope, q_rope, kv_pool, N, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
-                         B, q_len, H, scale_log2, ws_ml, ws_acc};
+                         B, q_len, H, scale_log2, ws_ml, ws_acc, ws_top};
   const Split sp = decode_unit(a.B, nsplit, n_rt);
   if (!sp.valid) return;
   const int b = sp.b, s = sp.s;
@@ -930,10 +875,10 @@ verify_partial_balanced_kernel(const __bf16* __restrict__ q_nope, const __bf16* 
                                const int32_t* __restrict__ mask_indptr, int B, int q_len, int H,
                                float scale_log2, int units, int n_rt, int fused_plan, int4* __restrict__ split_info,
                                int* __restrict__ split_start, float2* __restrict__ ws_ml,
-                               float* __restrict__ ws_acc) {
+                               float* __restrict__ ws_acc, int4* __restrict__ ws_top) {
   PARTIAL_LDS_DECL
   const PartialArgs a = {q_nope, q_rope, kv_pool, N, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
-                         B, q_len, H, scale_log2, ws_ml, ws_acc};
+                         B, q_len, H, scale_log2, ws_ml, ws_acc, ws_top};
   const int xcd = (int)(blockIdx.x % 8), k = (int)(blockIdx.x / 8);
   const int j = xcd + 8 * (k / n_rt), rt = k % n_rt;
   if (j >= units) return;
@@ -972,7 +917,8 @@ constexpr int combine_block_waves() { return kWaves == 1 ? 4 : kWaves; }
 
 template <bool kBalanced, int kWaves>
 __global__ void __launch_bounds__(combine_block_waves<kWaves>() * 64)
-verify_combine_kernel(const float2* __restrict__ ws_ml, const float* __restrict__ ws_acc, int B, int R,
+verify_combine_kernel(const float2* __restrict__ ws_ml, const float* __restrict__ ws_acc,
+                      const int4* __restrict__ ws_top, int B, int R,
                       int nsplit_or_units, const int* __restrict__ split_start, __bf16* __restrict__ out,
                       float* __restrict__ lse) {
   constexpr int kRed = kWaves > 1 ? kWaves : 2;
@@ -1055,6 +1001,41 @@ verify_combine_kernel(const float2* __restrict__ ws_ml, const float* __restrict_
       den += red_den[k];
     }
   }
+  // Exact top probabilities: a split whose top column holds at least 1/32 of the row's final sum gets
+  // w_s (p - bf16(p)) times that column's value row added (the partial kernels rounded p to bf16 for
+  // the PV product). A column below that share moves the output by under 2^-14 of its value row.
+  // Lane k checks splits k, k + 64, ...; the (rare) qualifying ones are applied one at a time by
+  // the whole wave, lane k loading values 8k .. 8k+7 of the row.
+  const int4* top = ws_top + first * R + r;
+  for (int s0 = 0; s0 < nsplit; s0 += 64) {
+    const int s = s0 + lane;
+    float coef = 0.0f;
+    bool take = false;
+    int4 t = make_int4(0, 0, 0, 0);
+    if (s < nsplit) {
+      const float2 st = ml[(size_t)s * R];
+      if (st.x != -INFINITY) {
+        t = top[(size_t)s * R];
+        const float p = __int_as_float(t.x);
+        const float wgt = __builtin_amdgcn_exp2f(st.x - M);  // the weight the accumulator got above
+        take = 32.0f * (p * wgt) >= den;
+        coef = wgt * (p - (float)(__bf16)p);
+      }
+    }
+    uint64_t pick = __ballot(take);
+    while (pick) {
+      const int k = __ffsll((long long)pick) - 1;
+      pick &= pick - 1;
+      const float c = __shfl(coef, k, 64);
+      const uint64_t vrow = ((uint64_t)(uint32_t)__shfl(t.z, k, 64) << 32) | (uint32_t)__shfl(t.y, k, 64);
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint8_t*>(vrow) + lane * 16);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc0[q] += c * (float)v[q];
+        acc1[q] += c * (float)v[4 + q];
+      }
+    }
+  }
   const float inv = 1.0f / den;
   bf16x8 res;
 #pragma unroll
@@ -1073,14 +1054,17 @@ constexpr long long kCombineFewRows = 512;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Per partial row: (m, l), the 512 accumulators, and the top record {exact top probability (float
+// bits), value-row address low, high, 0}; each region 256-byte aligned.
 struct WorkspaceLayout {
-  size_t ml_bytes, acc_bytes;
+  size_t ml_bytes, acc_bytes, top_bytes;
 };
 
 WorkspaceLayout workspace_layout(int B, int q_len, int H, int nsplit) {
   const size_t rows = (size_t)B * nsplit * q_len * H;
   return {align_up(rows * sizeof(float2), MLA_VERIFY_WORKSPACE_ALIGN),
-          align_up(rows * kLatent * sizeof(float), MLA_VERIFY_WORKSPACE_ALIGN)};
+          align_up(rows * kLatent * sizeof(float), MLA_VERIFY_WORKSPACE_ALIGN),
+          align_up(rows * sizeof(int4), MLA_VERIFY_WORKSPACE_ALIGN)};
 }
 
 bool sizes_ok(int B, int q_len, int H) {
@@ -1089,17 +1073,18 @@ bool sizes_ok(int B, int q_len, int H) {
   return rows <= (1LL << 24) && (long long)B * rows <= (1LL << 30);
 }
 
-// Balanced workspace: the plan (split_info int32x4 [units], split_start int32 [B + 1]), then (m, l)
-// and accumulators for `units` partial row blocks, each region 256-byte aligned.
+// Balanced workspace: the plan (split_info int32x4 [units], split_start int32 [B + 1]), then (m, l),
+// accumulators and top records for `units` partial row blocks, each region 256-byte aligned.
 struct BalancedLayout {
-  size_t plan_bytes, ml_bytes, acc_bytes;
+  size_t plan_bytes, ml_bytes, acc_bytes, top_bytes;
 };
 
 BalancedLayout balanced_layout(int B, int q_len, int H, int units) {
   const size_t rows = (size_t)units * q_len * H;
   return {align_up((size_t)units * sizeof(int4) + (size_t)(B + 1) * sizeof(int), MLA_VERIFY_WORKSPACE_ALIGN),
           align_up(rows * sizeof(float2), MLA_VERIFY_WORKSPACE_ALIGN),
-          align_up(rows * kLatent * sizeof(float), MLA_VERIFY_WORKSPACE_ALIGN)};
+          align_up(rows * kLatent * sizeof(float), MLA_VERIFY_WORKSPACE_ALIGN),
+          align_up(rows * sizeof(int4), MLA_VERIFY_WORKSPACE_ALIGN)};
 }
 
 bool balanced_sizes_ok(int B, int q_len, int H, int units) {
@@ -1112,13 +1097,13 @@ bool balanced_sizes_ok(int B, int q_len, int H, int units) {
 extern "C" size_t mla_verify_attn_workspace_size(int B, int q_len, int H, int nsplit) {
   if (!sizes_ok(B, q_len, H) || nsplit < 1 || nsplit > MLA_VERIFY_MAX_NSPLIT) return 0;
   const WorkspaceLayout lay = workspace_layout(B, q_len, H, nsplit);
-  return lay.ml_bytes + lay.acc_bytes;
+  return lay.ml_bytes + lay.acc_bytes + lay.top_bytes;
 }
 
 extern "C" size_t mla_verify_attn_balanced_workspace_size(int B, int q_len, int H, int units) {
   if (!balanced_sizes_ok(B, q_len, H, units)) return 0;
   const BalancedLayout lay = balanced_layout(B, q_len, H, units);
-  return lay.plan_bytes + lay.ml_bytes + lay.acc_bytes;
+  return lay.plan_bytes + lay.ml_bytes + lay.acc_bytes + lay.top_bytes;
 }
 
 extern "C" const char* mla_verify_status_string(int status) {
@@ -1138,6 +1123,7 @@ namespace {
 struct Launch {
   float2* ws_ml;
   float* ws_acc;
+  int4* ws_top;
   int R;
 };
 
@@ -1152,8 +1138,9 @@ int check_common(int B, int q_len, int H, int nsplit, const void* workspace, siz
 
 Launch split_workspace(void* workspace, int B, int q_len, int H, int nsplit) {
   const WorkspaceLayout lay = workspace_layout(B, q_len, H, nsplit);
-  return {static_cast<float2*>(workspace),
-          reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + lay.ml_bytes), q_len * H};
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  return {reinterpret_cast<float2*>(w), reinterpret_cast<float*>(w + lay.ml_bytes),
+          reinterpret_cast<int4*>(w + lay.ml_bytes + lay.acc_bytes), q_len * H};
 }
 
 int launch_partial(const void* q_nope, const void* q_rope, const void* kv_pool, int64_t N,
@@ -1166,10 +1153,10 @@ int launch_partial(const void* q_nope, const void* q_rope, const void* kv_pool, 
   const PartialArgs a = {static_cast<const __bf16*>(q_nope), static_cast<const __bf16*>(q_rope),
                          static_cast<const uint8_t*>(kv_pool), (int)N, kv_indptr, kv_indices, out_cache_loc,
                          custom_mask, mask_indptr, B, q_len, H, scale * 1.44269504088896340736f,
-                         ws.ws_ml, ws.ws_acc};
+                         ws.ws_ml, ws.ws_acc, ws.ws_top};
   hipLaunchKernelGGL(verify_partial_kernel, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, a.q_nope, a.q_rope,
                      a.kv_pool, a.N, a.kv_indptr, a.kv_indices, a.out_cache_loc, a.custom_mask, a.mask_indptr, a.B,
-                     a.q_len, a.H, a.scale_log2, nsplit, n_rt, a.ws_ml, a.ws_acc);
+                     a.q_len, a.H, a.scale_log2, nsplit, n_rt, a.ws_ml, a.ws_acc, a.ws_top);
   return hipGetLastError() == hipSuccess ? MLA_VERIFY_OK : MLA_VERIFY_ERR_LAUNCH;
 }
 
@@ -1177,13 +1164,13 @@ int launch_combine(const Launch& ws, int B, int nsplit, void* out, float* lse, h
   const long long crows = (long long)B * ws.R;
   if (crows >= kCombineManyRows)
     hipLaunchKernelGGL((verify_combine_kernel<false, 1>), dim3((unsigned)((crows + 3) / 4)), dim3(256), 0, stream,
-                       ws.ws_ml, ws.ws_acc, B, ws.R, nsplit, nullptr, static_cast<__bf16*>(out), lse);
+                       ws.ws_ml, ws.ws_acc, ws.ws_top, B, ws.R, nsplit, nullptr, static_cast<__bf16*>(out), lse);
   else if (crows >= kCombineFewRows)
     hipLaunchKernelGGL((verify_combine_kernel<false, 4>), dim3((unsigned)crows), dim3(256), 0, stream, ws.ws_ml,
-                       ws.ws_acc, B, ws.R, nsplit, nullptr, static_cast<__bf16*>(out), lse);
+                       ws.ws_acc, ws.ws_top, B, ws.R, nsplit, nullptr, static_cast<__bf16*>(out), lse);
   else
     hipLaunchKernelGGL((verify_combine_kernel<false, 16>), dim3((unsigned)crows), dim3(1024), 0, stream, ws.ws_ml,
-                       ws.ws_acc, B, ws.R, nsplit, nullptr, static_cast<__bf16*>(out), lse);
+                       ws.ws_acc, ws.ws_top, B, ws.R, nsplit, nullptr, static_cast<__bf16*>(out), lse);
   return hipGetLastError() == hipSuccess ? MLA_VERIFY_OK : MLA_VERIFY_ERR_LAUNCH;
 }
 
@@ -1192,6 +1179,7 @@ struct BalancedLaunch {
   int4* split_info;
   float2* ws_ml;
   float* ws_acc;
+  int4* ws_top;
   int R;
 };
 
@@ -1210,7 +1198,7 @@ BalancedLaunch balanced_workspace(void* workspace, int B, int q_len, int H, int 
   uint8_t* w = static_cast<uint8_t*>(workspace);
   return {reinterpret_cast<int*>(w + (size_t)units * sizeof(int4)), reinterpret_cast<int4*>(w),
           reinterpret_cast<float2*>(w + lay.plan_bytes), reinterpret_cast<float*>(w + lay.plan_bytes + lay.ml_bytes),
-          q_len * H};
+          reinterpret_cast<int4*>(w + lay.plan_bytes + lay.ml_bytes + lay.acc_bytes), q_len * H};
 }
 
 int launch_balanced_partial(const void* q_nope, const void* q_rope, const void* kv_pool, int64_t N,
@@ -1230,7 +1218,7 @@ int launch_balanced_partial(const void* q_nope, const void* q_rope, const void* 
                      static_cast<const __bf16*>(q_nope), static_cast<const __bf16*>(q_rope),
                      static_cast<const uint8_t*>(kv_pool), (int)N, kv_indptr, kv_indices, out_cache_loc, custom_mask,
                      mask_indptr, B, q_len, H, scale * 1.44269504088896340736f, units, n_rt, fused,
-                     (int4*)ws.split_info, (int*)ws.split_start, ws.ws_ml, ws.ws_acc);
+                     (int4*)ws.split_info, (int*)ws.split_start, ws.ws_ml, ws.ws_acc, ws.ws_top);
   return hipGetLastError() == hipSuccess ? MLA_VERIFY_OK : MLA_VERIFY_ERR_LAUNCH;
 }
 
@@ -1238,13 +1226,13 @@ int launch_balanced_combine(const BalancedLaunch& ws, int B, int units, void* ou
   const long long crows = (long long)B * ws.R;
   if (crows >= kCombineManyRows)
     hipLaunchKernelGGL((verify_combine_kernel<true, 1>), dim3((unsigned)((crows + 3) / 4)), dim3(256), 0, stream,
-                       ws.ws_ml, ws.ws_acc, B, ws.R, units, (const int*)ws.split_start, static_cast<__bf16*>(out), lse);
+                       ws.ws_ml, ws.ws_acc, ws.ws_top, B, ws.R, units, (const int*)ws.split_start, static_cast<__bf16*>(out), lse);
   else if (crows >= kCombineFewRows)
     hipLaunchKernelGGL((verify_combine_kernel<true, 4>), dim3((unsigned)crows), dim3(256), 0, stream, ws.ws_ml,
-                       ws.ws_acc, B, ws.R, units, (const int*)ws.split_start, static_cast<__bf16*>(out), lse);
+                       ws.ws_acc, ws.ws_top, B, ws.R, units, (const int*)ws.split_start, static_cast<__bf16*>(out), lse);
   else
     hipLaunchKernelGGL((verify_combine_kernel<true, 16>), dim3((unsigned)crows), dim3(1024), 0, stream, ws.ws_ml,
-                       ws.ws_acc, B, ws.R, units, (const int*)ws.split_start, static_cast<__bf16*>(out), lse);
+                       ws.ws_acc, ws.ws_top, B, ws.R, units, (const int*)ws.split_start, static_cast<__bf16*>(out), lse);
   return hipGetLastError() == hipSuccess ? MLA_VERIFY_OK : MLA_VERIFY_ERR_LAUNCH;
 }
 
