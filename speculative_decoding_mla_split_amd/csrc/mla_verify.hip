@@ -817,45 +817,88 @@ verify_plan_kernel(const int32_t* __restrict__ kv_indptr, int B, int q_len, int 
   }
 }
 
+// Wave-wide sum / max of 32-bit values as a wave-uniform result, and an inclusive prefix sum over the
+// 64 lanes: DPP moves inside each 16-lane row (rotations for the reductions, shifts that bring in 0
+// for the scan), then the four row results through readlane, with no LDS round trip.
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, false);  // row_ror:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x122, 0xF, 0xF, false);  // row_ror:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x121, 0xF, 0xF, false);  // row_ror:1
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) + __builtin_amdgcn_readlane(v, 32) +
+         __builtin_amdgcn_readlane(v, 48);
+}
+__device__ __forceinline__ int wave_max_i32(int v) {
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x122, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x121, 0xF, 0xF, false));
+  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+__device__ __forceinline__ int wave_incl_scan_i32(int x, int lane) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+            r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = lane >> 4;
+  return x + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
+
 // The same plan for batches of at most 64 requests, computed by one wave inside the partial kernel
 // (lane b holds request b) for split j alone: {request, first column, end column, 0}, or
-// {-1, 0, 0, 0} when the plan leaves split j unused. Every wave of every workgroup computes it (a
-// dozen search steps of wave reductions, cheaper than a separate launch in front of the kernel),
-// with the integer arithmetic of verify_plan_kernel, so the two give identical plans. Lanes b < B
-// return their request's running split count in *start_excl and *start_incl.
+// {-1, 0, 0, 0} when the plan leaves split j unused. Every wave of every workgroup computes it (a few
+// search steps of wave reductions, cheaper than a separate launch in front of the kernel). The
+// result is the same C, n_b and ranges as verify_plan_kernel's: the count function is monotone in C,
+// so searching a narrower interval that contains the smallest feasible C finds the same one, here
+// [ceil(total / units), ceil(total / (units - B))] (below the first bound the count exceeds
+// total / C > units; at the second it is at most total / C + B <= units), capped by the largest T_b.
+// Counts are 32-bit while every T_b < 2^25 (64 requests then total under 2^31 tiles); longer
+// requests (prefixes beyond 2^30 columns) take a 64-bit search over [1, max T_b]. Lanes b < B return
+// their request's running split count in *start_incl.
 constexpr int kFusedPlanMaxB = 64;
 __device__ __forceinline__ int4 plan_split_wave(const int32_t* __restrict__ kv_indptr, int B, int q_len, int units,
-                                                int j, int lane, int* start_excl, int* start_incl) {
+                                                int j, int lane, int* start_incl) {
   int T = 0, Lb = 0;
   if (lane < B) {
     const long long L = max((long long)kv_indptr[lane + 1] - (long long)kv_indptr[lane], 0LL) + q_len;
     T = (int)((L + kTile - 1) / kTile);
     Lb = (int)L;
   }
-  int tmax = max(T, 1);
-  for (int d = 32; d >= 1; d >>= 1) tmax = max(tmax, __shfl_xor(tmax, d, 64));
-  unsigned lo = 1, hi = (unsigned)tmax;
-  while (lo < hi) {
-    const unsigned mid = (lo + hi) / 2;
-    const long long cnt = lane < B ? (long long)(((unsigned)T + mid - 1) / mid) : 0;
-    if (wave_sum(cnt) <= units) hi = mid; else lo = mid + 1;
+  const int tmax = max(wave_max_i32(T), 1);
+  unsigned C;
+  if (tmax < (1 << 25)) {
+    const int total = wave_sum_i32(T);
+    int lo = max((total + units - 1) / units, 1);
+    int hi = units > B ? min(tmax, (total + (units - B) - 1) / (units - B)) : tmax;
+    lo = min(lo, hi);
+    while (lo < hi) {  // wave-uniform bounds: a scalar loop
+      const int mid = (lo + hi) >> 1;
+      const int cnt = wave_sum_i32((int)(((unsigned)T + (unsigned)mid - 1) / (unsigned)mid));
+      if (cnt <= units) hi = mid; else lo = mid + 1;
+    }
+    C = (unsigned)lo;
+  } else {
+    unsigned lo = 1, hi = (unsigned)tmax;
+    while (lo < hi) {
+      const unsigned mid = (lo + hi) / 2;
+      const long long cnt = (long long)(((unsigned)T + mid - 1) / mid);
+      if (wave_sum(cnt) <= units) hi = mid; else lo = mid + 1;
+    }
+    C = lo;
   }
-  const unsigned C = lo;
   const int n = lane < B ? (int)(((unsigned)T + C - 1) / C) : 0;
-  int incl = n;
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += y;
-  }
+  const int incl = wave_incl_scan_i32(n, lane);
   const int excl = incl - n;
-  *start_excl = excl;
   *start_incl = incl;
   const unsigned long long own = __ballot(lane < B && excl <= j && j < incl);
   if (own == 0) return make_int4(-1, 0, 0, 0);
   const int l = __ffsll((long long)own) - 1;
-  const int s_l = j - __shfl(excl, l, 64), n_l = __shfl(n, l, 64);
-  const long long T_l = __shfl(T, l, 64);
-  const int L_l = __shfl(Lb, l, 64);
+  const int s_l = j - __builtin_amdgcn_readlane(excl, l), n_l = __builtin_amdgcn_readlane(n, l);
+  const long long T_l = __builtin_amdgcn_readlane(T, l);
+  const int L_l = __builtin_amdgcn_readlane(Lb, l);
   const int c0 = (int)((long long)s_l * T_l / n_l) * kTile;
   const int c1 = min(L_l, (int)((long long)(s_l + 1) * T_l / n_l) * kTile);
   return make_int4(l, c0, c1, 0);
@@ -885,8 +928,8 @@ verify_partial_balanced_kernel(const __bf16* __restrict__ q_nope, const __bf16* 
   int4 info;  // {request, first column, end column}
   if (fused_plan) {
     const int lane = threadIdx.x & 63;
-    int excl, incl;
-    info = plan_split_wave(kv_indptr, B, q_len, units, j, lane, &excl, &incl);
+    int incl;
+    info = plan_split_wave(kv_indptr, B, q_len, units, j, lane, &incl);
     if (threadIdx.x < 64) {
       if (rt == 0 && lane == 0) split_info[j] = info;
       if (blockIdx.x == 0) {
