@@ -279,6 +279,44 @@ def test_top_probability_restored_within_half_ulp(balanced, nsplit):
     assert excess.max() <= 0, f"{int((excess > 0).sum())} outputs beyond half a bf16 ulp"
 
 
+@pytest.mark.parametrize("balanced,nsplit", [(False, 2), (True, 4)])
+def test_two_dominant_columns_in_different_splits(balanced, nsplit):
+    """Two dominant prefix columns per request, one in each of the request's two splits and each
+    behind its split's first tile, with nearly equal scores: both splits' top columns hold about half
+    of the row's sum, so the combine restores both exact probabilities; the output must again be the
+    fp64 result within half a bf16 ulp. Splits: per-request nsplit 2 gives request 0 columns
+    [0, 160) and [160, 304), request 1 [0, 128) and [128, 194); the balanced plan with 4 units gives
+    request 0 the same and request 1 [0, 96) and [96, 194). The kernel stores each score's element
+    index in its 4 lowest mantissa bits (a change of up to ~1.7e-5 in a probability here): with one
+    dominant column that cancels in p / l, with two it moves their relative weights, so the bound
+    adds 1e-5 of the row's largest output (the uncorrected arithmetic still misses it on 5929 of
+    32768 outputs, by up to 1.3e-3)."""
+    _say(f"[top] two dominant columns balanced={balanced} nsplit={nsplit}")
+    inp = _mk(42, (300, 190), 4, 8)
+    rng = np.random.default_rng(8)
+    u = rng.standard_normal(576)
+    q = u + 0.3 * rng.standard_normal((inp.B, inp.q_len, inp.H, 576))
+    inp.q_nope[:] = W.bf16_from_f32(q[..., :512].astype(np.float32))
+    inp.q_rope[:] = W.bf16_from_f32(q[..., 512:].astype(np.float32))
+    gam = 10.0 * math.sqrt(192.0) / float(u @ u)
+    inp.ref_rows[:] = 0
+    pos = 0
+    for b, cols in enumerate(((100, 250), (70, 180))):
+        for k, col in enumerate(cols):
+            row = gam * u + (0.05 * k) * rng.standard_normal(576)  # the second one slightly different
+            inp.ref_rows[pos + col] = W.bf16_from_f32(row.astype(np.float32))
+        pos += inp.prefixes[b] + inp.q_len
+    call = DeviceCall(inp)
+    call.run(nsplit, balanced=balanced)
+    got_out, got_lse = call.host()
+    ref_out, ref_lse = _oracle_full(inp)
+    compare(got_out, got_lse, ref_out, ref_lse, "two dominant columns")
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref_out), 1e-30))) - 7)
+    row_max = np.abs(ref_out).max(axis=-1, keepdims=True)
+    excess = np.abs(got_out - ref_out) - (0.5 * ulp + 1e-5 * row_max)
+    assert excess.max() <= 0, f"{int((excess > 0).sum())} outputs beyond half a bf16 ulp"
+
+
 def test_deterministic_and_workspace_reuse():
     _say("[det] repeated calls bit-identical")
     inp = _mk(37, (2000,), 9, 64)
