@@ -241,7 +241,7 @@ def measured_traffic(workload, split_tag):
         return None, "kernel changed since the counters were taken"
     fetch = t["fetch_kib_per_dispatch"] * 1024 / t["copy_fetch_factor"]
     write = t["write_kib_per_dispatch"] * 1024 / t["copy_write_factor"]
-    return fetch + write, path
+    return fetch + write, os.path.relpath(path, ROOT)
 
 
 def copy_calibration(gib: float, reps: int):
