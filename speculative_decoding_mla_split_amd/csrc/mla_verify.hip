@@ -947,12 +947,21 @@ verify_partial_balanced_kernel(const __bf16* __restrict__ q_nope, const __bf16* 
 }
 
 // kWaves waves per query row (b, r): weights w_s = 2^(m_s - M) over the non-empty partials,
-// out = sum w_s acc_s / sum w_s l_s, lse = (M + log2 sum w_s l_s) * ln 2. Lane k owns output columns
-// [8k, 8k+8); wave w of a row takes splits w, w + kWaves, ..., 8 (4 with 16 waves) at a time with
-// all their loads issued together, and waves 1.. hand their sums to wave 0 through LDS. One wave per
-// row (4 rows per workgroup) suits many rows (the ragged 185k batch, 4096 rows); more waves per row
-// keep the chip busy when there are few rows and many splits (72 rows x 256 splits with one wave each
-// left most CUs idle and walked 256 splits serially: 95 us, against 11 us with sixteen waves).
+// out = sum w_s acc_s / sum w_s l_s, lse = (M + log2 sum w_s l_s) * ln 2. One wave per row (4 rows
+// per workgroup) suits many rows (the ragged 185k batch, 4096 rows); more waves per row keep the chip
+// busy when there are few rows and many splits (72 rows x 256 splits with one wave each left most
+// CUs idle and walked 256 splits serially: 95 us, against 11 us with sixteen waves). The kernel is
+// bound by memory round trips, so it keeps them few:
+//  1. lane k of wave w reads the (m, l) pair and top record of split w*64 + k (and the maxima of
+//     splits further on): the row max M;
+//  2. lane k owns output columns [8k, 8k+8); wave w takes splits w, w + kWaves, ..., 4 at a time,
+//     every (m, l) and accumulator load of a batch issued together (an empty
+//     split's accumulator was never written: it is read, then discarded by a select);
+//  3. the sum is reduced over the row's waves; each wave adds back, for its own splits whose top
+//     column holds at least 1/32 of the row's sum, w_s (p - bf16(p)) times that column's value row
+//     (the partial kernels rounded p to bf16 for the PV product; a column below that share moves the
+//     output by under 2^-14 of its value row), from the records it read in step 1; waves 1.. hand
+//     their accumulators to wave 0 through LDS.
 // kBalanced: the partials of request b are blocks split_start[b] .. split_start[b+1] - 1 (the plan);
 // otherwise the nsplit blocks b * nsplit .. b * nsplit + nsplit - 1.
 template <int kWaves>
@@ -967,7 +976,7 @@ verify_combine_kernel(const float2* __restrict__ ws_ml, const float* __restrict_
   constexpr int kRed = kWaves > 1 ? kWaves : 2;
   __shared__ float red_m[kRed];
   __shared__ f32x4 red_acc[kRed - 1][2][64];
-  __shared__ float red_den[kRed - 1];
+  __shared__ float red_den[kRed];
   const int lane = threadIdx.x & 63;
   const int w = kWaves == 1 ? 0 : (int)(threadIdx.x >> 6);  // wave of the row
   const long row = kWaves == 1 ? (long)blockIdx.x * 4 + (threadIdx.x >> 6) : (long)blockIdx.x;
@@ -983,9 +992,13 @@ verify_combine_kernel(const float2* __restrict__ ws_ml, const float* __restrict_
     first = (size_t)b * nsplit;
   }
   const float2* ml = ws_ml + first * R + r;
-  // M over the splits: each lane of the row's waves reads every (64 kWaves)-th split, then a max
-  float M = -INFINITY;
-  for (int s = w * 64 + lane; s < nsplit; s += kWaves * 64) M = fmaxf(M, ml[(size_t)s * R].x);
+  const int4* top = ws_top + first * R + r;
+  // 1. split w*64 + lane: (m, l) and top record in registers; the max over every split
+  const int s_own = w * 64 + lane;
+  const float2 st_own = s_own < nsplit ? ml[(size_t)s_own * R] : make_float2(-INFINITY, 0.0f);
+  const int4 top_own = s_own < nsplit ? top[(size_t)s_own * R] : make_int4(0, 0, 0, 0);
+  float M = st_own.x;
+  for (int s = s_own + kWaves * 64; s < nsplit; s += kWaves * 64) M = fmaxf(M, ml[(size_t)s * R].x);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   if constexpr (kWaves > 1) {
@@ -1003,68 +1016,54 @@ verify_combine_kernel(const float2* __restrict__ ws_ml, const float* __restrict_
     }
     return;
   }
+  // 2. weighted accumulators and sum over this wave's splits
   f32x4 acc0 = {}, acc1 = {};
   float den = 0.0f;
   const float* base = ws_acc + (first * R + r) * kLatent + lane * 8;
   const size_t split_stride = (size_t)R * kLatent;
-  constexpr int kU = kWaves >= 16 ? 4 : 8;  // splits in flight per wave (the 16-wave form has 128 registers)
+  constexpr int kU = 4;  // splits per batch (8 measured slower: the registers cut occupancy to 3 waves)
   for (int s0 = w; s0 < nsplit; s0 += kWaves * kU) {
-    float wgt[kU];
+    float2 st[kU];
     f32x4 x0[kU], x1[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int s = s0 + kWaves * u;
-      const float2 st = s < nsplit ? ml[(size_t)s * R] : make_float2(-INFINITY, 0.0f);
-      // empty or fully masked split: weight 0 and its accumulator is never read
-      const bool live = st.x != -INFINITY;
-      wgt[u] = live ? __builtin_amdgcn_exp2f(st.x - M) : 0.0f;
-      den += live ? wgt[u] * st.y : 0.0f;
-      const f32x4* src = reinterpret_cast<const f32x4*>(base + (size_t)(live ? s : 0) * split_stride);
-      x0[u] = live ? src[0] : f32x4{};
-      x1[u] = live ? src[1] : f32x4{};
+      const bool valid = s < nsplit;
+      st[u] = valid ? ml[(size_t)s * R] : make_float2(-INFINITY, 0.0f);
+      const f32x4* src = reinterpret_cast<const f32x4*>(base + (size_t)(valid ? s : 0) * split_stride);
+      x0[u] = src[0];
+      x1[u] = src[1];
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      acc0 += wgt[u] * x0[u];
-      acc1 += wgt[u] * x1[u];
+      const bool live = st[u].x != -INFINITY;  // empty or fully masked split: weight 0, data unused
+      const float wgt = live ? __builtin_amdgcn_exp2f(st[u].x - M) : 0.0f;
+      den += live ? wgt * st[u].y : 0.0f;
+      acc0 += live ? wgt * x0[u] : f32x4{};
+      acc1 += live ? wgt * x1[u] : f32x4{};
     }
   }
+  // 3. the row's sum, then the exact top probabilities of this wave's splits
+  float den_row = den;
   if constexpr (kWaves > 1) {
-    if (w > 0) {
-      red_acc[w - 1][0][lane] = acc0;
-      red_acc[w - 1][1][lane] = acc1;
-      if (lane == 0) red_den[w - 1] = den;
-    }
+    if (lane == 0) red_den[w] = den;
     __syncthreads();
-    if (w != 0) return;
+    den_row = red_den[0];
 #pragma unroll
-    for (int k = 0; k < kWaves - 1; ++k) {
-      acc0 += red_acc[k][0][lane];
-      acc1 += red_acc[k][1][lane];
-      den += red_den[k];
-    }
+    for (int k = 1; k < kWaves; ++k) den_row += red_den[k];
   }
-  // Exact top probabilities: a split whose top column holds at least 1/32 of the row's final sum gets
-  // w_s (p - bf16(p)) times that column's value row added (the partial kernels rounded p to bf16 for
-  // the PV product). A column below that share moves the output by under 2^-14 of its value row.
-  // Lane k checks splits k, k + 64, ...; the (rare) qualifying ones are applied one at a time by
-  // the whole wave, lane k loading values 8k .. 8k+7 of the row.
-  const int4* top = ws_top + first * R + r;
-  for (int s0 = 0; s0 < nsplit; s0 += 64) {
-    const int s = s0 + lane;
-    float coef = 0.0f;
-    bool take = false;
-    int4 t = make_int4(0, 0, 0, 0);
-    if (s < nsplit) {
-      const float2 st = ml[(size_t)s * R];
-      if (st.x != -INFINITY) {
-        t = top[(size_t)s * R];
-        const float p = __int_as_float(t.x);
-        const float wgt = __builtin_amdgcn_exp2f(st.x - M);  // the weight the accumulator got above
-        take = 32.0f * (p * wgt) >= den;
-        coef = wgt * (p - (float)(__bf16)p);
-      }
+  for (int s = s_own; s - lane < nsplit; s += kWaves * 64) {  // wave-uniform bound
+    float2 st = st_own;
+    int4 t = top_own;
+    if (s != s_own && s < nsplit) {  // splits past the first 64 kWaves (rare): read their records
+      st = ml[(size_t)s * R];
+      t = top[(size_t)s * R];
     }
+    const bool live = s < nsplit && st.x != -INFINITY;
+    const float p = __int_as_float(t.x);
+    const float wgt = live ? __builtin_amdgcn_exp2f(st.x - M) : 0.0f;  // the weight the accumulator got
+    const bool take = live && 32.0f * (p * wgt) >= den_row;
+    const float coef = wgt * (p - (float)(__bf16)p);
     uint64_t pick = __ballot(take);
     while (pick) {
       const int k = __ffsll((long long)pick) - 1;
@@ -1079,7 +1078,20 @@ verify_combine_kernel(const float2* __restrict__ ws_ml, const float* __restrict_
       }
     }
   }
-  const float inv = 1.0f / den;
+  if constexpr (kWaves > 1) {
+    if (w > 0) {
+      red_acc[w - 1][0][lane] = acc0;
+      red_acc[w - 1][1][lane] = acc1;
+    }
+    __syncthreads();
+    if (w != 0) return;
+#pragma unroll
+    for (int k = 0; k < kWaves - 1; ++k) {
+      acc0 += red_acc[k][0][lane];
+      acc1 += red_acc[k][1][lane];
+    }
+  }
+  const float inv = 1.0f / den_row;
   bf16x8 res;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -1087,7 +1099,7 @@ verify_combine_kernel(const float2* __restrict__ ws_ml, const float* __restrict_
     res[4 + k] = (__bf16)(acc1[k] * inv);
   }
   *o = res;
-  if (lane == 0) lse[row] = (M + log2f(den)) * 0.69314718055994530942f;
+  if (lane == 0) lse[row] = (M + log2f(den_row)) * 0.69314718055994530942f;
 }
 
 // Row counts at which the combine uses one wave per row, else four, else sixteen (enough waves to fill
