@@ -366,3 +366,36 @@ def test_out_of_range_slot_is_memory_safe():
     call2.run(2)
     o2, l2 = call2.host()
     assert np.array_equal(o2[1], good_out[1]) and np.array_equal(l2[1], good_lse[1])
+
+
+@pytest.mark.parametrize("N", [3_728_270, 4_194_304])
+def test_pool_above_4gib_bit_identical(N):
+    """Pools whose byte size passes 2^32 (N * 1152 > 4 GiB) gather through 64-bit addresses, smaller
+    ones through 32-bit offsets from the pool base; both forms give the same bits as a small pool,
+    with the referenced rows at the very top of the large one."""
+    _say(f"[select] pool of {N} rows ({N * 1152 / 2**30:.2f} GiB), rows at its top")
+    inp_s = _mk(41, (900, 70), 9, 16, layout="scattered")
+    inp_w = copy.deepcopy(inp_s)
+    n_ref = len(inp_s.ref_slots)
+    perm = np.random.default_rng(42).permutation(n_ref)
+    top = (N - n_ref + perm).astype(np.int32)           # new slot of each referenced row
+    remap = {int(old): int(new) for old, new in zip(inp_s.ref_slots, top)}
+    inp_w.N = N
+    inp_w.ref_slots = top
+    inp_w.kv_indices = np.array([remap[int(x)] for x in inp_s.kv_indices], np.int32)
+    inp_w.out_cache_loc = np.array([remap[int(x)] for x in inp_s.out_cache_loc], np.int32)
+    assert inp_w.kv_indices.max() >= 3_700_000
+    small = DeviceCall(inp_s)
+    results = {}
+    for balanced in (False, True):
+        small.run(5, balanced=balanced)
+        results[balanced] = small.host()
+    del small
+    big = DeviceCall(inp_w)
+    for balanced in (False, True):
+        big.run(5, balanced=balanced)
+        ob, lb = big.host()
+        os_, ls_ = results[balanced]
+        assert np.array_equal(ob, os_) and np.array_equal(lb, ls_), f"balanced={balanced}"
+    del big
+    torch.cuda.empty_cache()
