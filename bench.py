@@ -122,7 +122,11 @@ class Workload:
             wall = (time.perf_counter() - t0) / steps * 1e6
         else:
             for k in range(steps):
-                scrub.fill_(k & 0xFF)  # evict the KV rows from L2 and the MALL (outside the events)
+                # evict the KV rows from L2 and the MALL outside the events: a 1 GiB read on the bench
+                # stream itself (a fill on another stream would run alongside the step, and a fill on
+                # this one would leave dirty lines whose write-back lands inside the step)
+                with torch.cuda.stream(stream):
+                    scrub.view(torch.int64).sum()
                 evs[k][0].record(stream)
                 self.partial(stream)
                 evs[k][1].record(stream)
