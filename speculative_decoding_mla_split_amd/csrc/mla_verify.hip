@@ -977,7 +977,8 @@ verify_partial_balanced_kernel(const __bf16* __restrict__ q_nope, const __bf16* 
 // out = sum w_s acc_s / sum w_s l_s, lse = (M + log2 sum w_s l_s) * ln 2. One wave per row (4 rows
 // per workgroup) suits many rows (the ragged 185k batch, 4096 rows); more waves per row keep the chip
 // busy when there are few rows and many splits (72 rows x 256 splits with one wave each left most
-// CUs idle and walked 256 splits serially: 95 us, against 11 us with sixteen waves). The kernel is
+// CUs idle and walked 256 splits serially: 95 us, against 11 us with sixteen waves; the quarter-row
+// kernel below takes that case now). The kernel is
 // bound by memory round trips, so it keeps them few:
 //  1. lane k of wave w reads the (m, l) pair and top record of split w*64 + k (and the maxima of
 //     splits further on): the row max M;
@@ -1129,8 +1130,156 @@ verify_combine_kernel(const float2* __restrict__ ws_ml, const float* __restrict_
   if (lane == 0) lse[row] = (M + log2f(den_row)) * 0.69314718055994530942f;
 }
 
-// Row counts at which the combine uses one wave per row, else four, else sixteen (enough waves to fill
-// 256 CUs either way).
+// Few rows: the same combine with four workgroups per row, one per 128-column quarter of the
+// output, so the pass over the partials spreads over four times as many CUs (72 rows x 256 splits
+// with one workgroup per row read their 38 MB from 72 CUs at ~2.8 TB/s). Lane (sq, cl) = (lane / 16,
+// lane % 16) takes columns [128 qc + 8 cl, +8) of the splits s = sq (mod 4) of its wave; the four lane
+// groups are summed by shuffles before the top-probability corrections and the cross-wave sum.
+constexpr int kQuarterWaves = 8;
+template <bool kBalanced>
+__global__ void __launch_bounds__(kQuarterWaves * 64)
+verify_combine_quarter_kernel(const float2* __restrict__ ws_ml, const float* __restrict__ ws_acc,
+                              const int4* __restrict__ ws_top, int B, int R, int nsplit_or_units,
+                              const int* __restrict__ split_start, __bf16* __restrict__ out,
+                              float* __restrict__ lse) {
+  __shared__ float red_m[kQuarterWaves];
+  __shared__ float red_den[kQuarterWaves];
+  __shared__ f32x4 red_acc[kQuarterWaves - 1][2][16];
+  const int lane = threadIdx.x & 63;
+  const int w = (int)(threadIdx.x >> 6);
+  const int sq = lane >> 4, cl = lane & 15;
+  const long row = (long)(blockIdx.x >> 2);
+  const int qc = (int)(blockIdx.x & 3);
+  if (row >= (long)B * R) return;
+  const long b = row / R, r = row % R;
+  size_t first;
+  int nsplit;
+  if constexpr (kBalanced) {
+    first = (size_t)split_start[b];
+    nsplit = split_start[b + 1] - split_start[b];
+  } else {
+    nsplit = nsplit_or_units;
+    first = (size_t)b * nsplit;
+  }
+  const float2* ml = ws_ml + first * R + r;
+  const int4* top = ws_top + first * R + r;
+  // 1. split w*64 + lane: (m, l) and top record in registers; the max over every split
+  const int s_own = w * 64 + lane;
+  const float2 st_own = s_own < nsplit ? ml[(size_t)s_own * R] : make_float2(-INFINITY, 0.0f);
+  const int4 top_own = s_own < nsplit ? top[(size_t)s_own * R] : make_int4(0, 0, 0, 0);
+  float M = st_own.x;
+  for (int s = s_own + kQuarterWaves * 64; s < nsplit; s += kQuarterWaves * 64) M = fmaxf(M, ml[(size_t)s * R].x);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  if (lane == 0) red_m[w] = M;
+  __syncthreads();
+  M = red_m[0];
+#pragma unroll
+  for (int k = 1; k < kQuarterWaves; ++k) M = fmaxf(M, red_m[k]);
+  const int col0 = 128 * qc + 8 * cl;
+  bf16x8* o = reinterpret_cast<bf16x8*>(out + (size_t)row * kLatent + col0);
+  if (M == -INFINITY) {
+    if (w == 0 && sq == 0) {
+      *o = bf16x8{};
+      if (cl == 0 && qc == 0) lse[row] = -INFINITY;
+    }
+    return;
+  }
+  // 2. weighted accumulators and sum over this lane group's splits
+  f32x4 acc0 = {}, acc1 = {};
+  float den = 0.0f;
+  const float* base = ws_acc + (first * R + r) * kLatent + col0;
+  const size_t split_stride = (size_t)R * kLatent;
+  constexpr int kU = 4;
+  constexpr int kStride = 4 * kQuarterWaves;  // splits between consecutive ones of a lane group
+  for (int s0 = 4 * w + sq; s0 < nsplit; s0 += kStride * kU) {
+    float2 st[kU];
+    f32x4 x0[kU], x1[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int s = s0 + kStride * u;
+      const bool valid = s < nsplit;
+      st[u] = valid ? ml[(size_t)s * R] : make_float2(-INFINITY, 0.0f);
+      const f32x4* src = reinterpret_cast<const f32x4*>(base + (size_t)(valid ? s : 0) * split_stride);
+      x0[u] = src[0];
+      x1[u] = src[1];
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const bool live = st[u].x != -INFINITY;  // empty or fully masked split: weight 0, data unused
+      const float wgt = live ? __builtin_amdgcn_exp2f(st[u].x - M) : 0.0f;
+      den += live ? wgt * st[u].y : 0.0f;
+      acc0 += live ? wgt * x0[u] : f32x4{};
+      acc1 += live ? wgt * x1[u] : f32x4{};
+    }
+  }
+  // the four lane groups of the wave: every lane ends with the wave's sums for its columns
+#pragma unroll
+  for (int d = 16; d <= 32; d <<= 1) {
+    den += __shfl_xor(den, d);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc0[k] += __shfl_xor(acc0[k], d);
+      acc1[k] += __shfl_xor(acc1[k], d);
+    }
+  }
+  // 3. the row's sum, then the exact top probabilities of this wave's splits (every lane group adds
+  // them to its identical copy; only group 0's is kept)
+  if (lane == 0) red_den[w] = den;
+  __syncthreads();
+  float den_row = red_den[0];
+#pragma unroll
+  for (int k = 1; k < kQuarterWaves; ++k) den_row += red_den[k];
+  for (int s = s_own; s - lane < nsplit; s += kQuarterWaves * 64) {  // wave-uniform bound
+    float2 st = st_own;
+    int4 t = top_own;
+    if (s != s_own && s < nsplit) {
+      st = ml[(size_t)s * R];
+      t = top[(size_t)s * R];
+    }
+    const bool live = s < nsplit && st.x != -INFINITY;
+    const float p = __int_as_float(t.x);
+    const float wgt = live ? __builtin_amdgcn_exp2f(st.x - M) : 0.0f;
+    const bool take = live && 32.0f * (p * wgt) >= den_row;
+    const float coef = wgt * (p - (float)(__bf16)p);
+    uint64_t pick = __ballot(take);
+    while (pick) {
+      const int k = __ffsll((long long)pick) - 1;
+      pick &= pick - 1;
+      const float c = __shfl(coef, k, 64);
+      const uint64_t vrow = ((uint64_t)(uint32_t)__shfl(t.z, k, 64) << 32) | (uint32_t)__shfl(t.y, k, 64);
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint8_t*>(vrow) + 2 * col0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc0[q] += c * (float)v[q];
+        acc1[q] += c * (float)v[4 + q];
+      }
+    }
+  }
+  if (w > 0 && sq == 0) {
+    red_acc[w - 1][0][cl] = acc0;
+    red_acc[w - 1][1][cl] = acc1;
+  }
+  __syncthreads();
+  if (w != 0 || sq != 0) return;
+#pragma unroll
+  for (int k = 0; k < kQuarterWaves - 1; ++k) {
+    acc0 += red_acc[k][0][cl];
+    acc1 += red_acc[k][1][cl];
+  }
+  const float inv = 1.0f / den_row;
+  bf16x8 res;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    res[k] = (__bf16)(acc0[k] * inv);
+    res[4 + k] = (__bf16)(acc1[k] * inv);
+  }
+  *o = res;
+  if (cl == 0 && qc == 0) lse[row] = (M + log2f(den_row)) * 0.69314718055994530942f;
+}
+
+// Row counts at which the combine uses one wave per row, else four, else eight per
+// quarter row (enough waves to fill 256 CUs either way).
 constexpr long long kCombineManyRows = 2048;
 constexpr long long kCombineFewRows = 512;
 
@@ -1256,8 +1405,9 @@ int launch_combine(const Launch& ws, int B, int nsplit, void* out, float* lse, h
     hipLaunchKernelGGL((verify_combine_kernel<false, 4>), dim3((unsigned)crows), dim3(256), 0, stream, ws.ws_ml,
                        ws.ws_acc, ws.ws_top, B, ws.R, nsplit, nullptr, static_cast<__bf16*>(out), lse);
   else
-    hipLaunchKernelGGL((verify_combine_kernel<false, 16>), dim3((unsigned)crows), dim3(1024), 0, stream, ws.ws_ml,
-                       ws.ws_acc, ws.ws_top, B, ws.R, nsplit, nullptr, static_cast<__bf16*>(out), lse);
+    hipLaunchKernelGGL((verify_combine_quarter_kernel<false>), dim3((unsigned)(4 * crows)), dim3(kQuarterWaves * 64), 0,
+                       stream, ws.ws_ml, ws.ws_acc, ws.ws_top, B, ws.R, nsplit, nullptr, static_cast<__bf16*>(out),
+                       lse);
   return hipGetLastError() == hipSuccess ? MLA_VERIFY_OK : MLA_VERIFY_ERR_LAUNCH;
 }
 
@@ -1319,8 +1469,9 @@ int launch_balanced_combine(const BalancedLaunch& ws, int B, int units, void* ou
     hipLaunchKernelGGL((verify_combine_kernel<true, 4>), dim3((unsigned)crows), dim3(256), 0, stream, ws.ws_ml,
                        ws.ws_acc, ws.ws_top, B, ws.R, units, (const int*)ws.split_start, static_cast<__bf16*>(out), lse);
   else
-    hipLaunchKernelGGL((verify_combine_kernel<true, 16>), dim3((unsigned)crows), dim3(1024), 0, stream, ws.ws_ml,
-                       ws.ws_acc, ws.ws_top, B, ws.R, units, (const int*)ws.split_start, static_cast<__bf16*>(out), lse);
+    hipLaunchKernelGGL((verify_combine_quarter_kernel<true>), dim3((unsigned)(4 * crows)), dim3(kQuarterWaves * 64), 0,
+                       stream, ws.ws_ml, ws.ws_acc, ws.ws_top, B, ws.R, units, (const int*)ws.split_start,
+                       static_cast<__bf16*>(out), lse);
   return hipGetLastError() == hipSuccess ? MLA_VERIFY_OK : MLA_VERIFY_ERR_LAUNCH;
 }
 
