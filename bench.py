@@ -139,13 +139,13 @@ class Workload:
         stepu = [evs[k][0].elapsed_time(evs[k][2]) * 1e3 for k in range(steps)]
         return wall, part, comb, stepu
 
-    def graph_us_per_step(self, stream, replays):
+    def graph_us_per_step(self, stream, replays, warmup=3):
         torch = self.torch
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(stream):
             with torch.cuda.graph(g, stream=stream):
                 self.step(stream)
-        for _ in range(3):
+        for _ in range(warmup):
             g.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -481,7 +481,8 @@ def main():
     print(f"[bench] timed {args.steps} steps: {wall:.1f} us/step", file=sys.stderr, flush=True)
     parity = wk.parity(args.parity_rows)
     check = None if args.no_next else measure_check(wk, stream)
-    graph_us = wk.graph_us_per_step(stream, max(args.steps, 20))
+    # as long a warmup as the eager steps: the first few dozen launches of the partial kernel run slower
+    graph_us = wk.graph_us_per_step(stream, max(args.steps, 20), warmup=args.warmup)
     part_s, comb_s = stats(part), stats(comb)
     alg = wk.alg
     value = alg["kv_bytes"] / (wall * 1e-6) / 1e9
