@@ -33,6 +33,20 @@ def _oracle_full(inp):
     return oracle.attn(*oracle.inputs_args(inp, pool, ki, oc))
 
 
+def test_balanced_largest_budget_mostly_idle_grid():
+    """The largest split budget on a small batch: the plan uses a few dozen of the 4096 splits, the
+    other workgroups of the 4096-workgroup grid leave at once, and the combine sees only the used
+    ones."""
+    units = 4096  # MLA_VERIFY_MAX_UNITS
+    inp = W.make_custom(np.random.default_rng(77), (900, 250), 9, 8)
+    _say(f"[balanced] largest budget units={units}")
+    call = DeviceCall(inp)
+    call.run(units, balanced=True)
+    got_out, got_lse = call.host()
+    ref_out, ref_lse = _oracle_full(inp)
+    compare(got_out, got_lse, ref_out, ref_lse, f"balanced units {units}")
+
+
 @pytest.mark.parametrize("seed,prefixes,q_len,H", SHAPES)
 @pytest.mark.parametrize("extra", [0, 1, 7, 61])
 def test_balanced_parity(seed, prefixes, q_len, H, extra):

@@ -91,7 +91,7 @@ def test_parity_ragged_185k_sampled():
     assert np.all(np.isfinite(got_out)) and np.all(np.isfinite(got_lse))
 
 
-@pytest.mark.parametrize("nsplit", [1, 2, 3, 16, 64, 128, "L", "L+5"])
+@pytest.mark.parametrize("nsplit", [1, 2, 3, 16, 64, 128, "L", "L+5", 1024])
 def test_split_invariance(nsplit):
     inp = _mk(20, (900, 250), 9, 8)
     L = max(inp.prefixes) + inp.q_len
