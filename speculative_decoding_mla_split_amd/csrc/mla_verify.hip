@@ -307,13 +307,17 @@ struct Bufs {
 //   3. mask + softmax numerators of the own block against its fixed reference max
 //   4. the bf16 probabilities of the own block go to LDS; after the barrier the partner's are read
 //   5. O^T of both blocks over the output half: each V fragment is read once and feeds two MFMAs
-// Loads: the step issues the 9 row loads of tile t+2 into ring buffer (t+2) % 3 (its previous
-// tile, t-1, every wave finished before the barrier that opened this step) and the metadata loads
-// of tile t+4, spread over the score and PV phases, where queued MFMAs keep the matrix pipe busy
-// while the wave waits to issue them (none in the softmax, which has no matrix work to hide behind).
-// A wave keeps only a few vector-memory instructions in flight, and one issued into a full queue
-// stalls the wave, so bunching the loads would idle the matrix pipe; a load has about two steps to
-// land.
+// Two barriers per step, and they also order the tile ring, so a step needs none of its own:
+//  - the score-exchange barrier of step t comes after every wave's PV of step t-1, so ring buffer
+//    (t+2) % 3, which held tile t-1, is free once it has passed;
+//  - before the probability-exchange barrier each wave waits for all its loads (vmcnt(0)): the row
+//    loads of tile t+1 it issued in step t-1; after that barrier tile t+1 is whole in LDS for every
+//    wave, ready for step t+1.
+// Hence the step issues the 9 row loads of tile t+2 and the metadata loads of tile t+4 in the PV
+// phase, between the MFMAs, after the probability-exchange barrier; a load has about one step to
+// land. (With a third barrier opening each step and the loads spread over the score and PV phases,
+// the step was 4% slower at the 185k batch; where the loads sit inside the step moved it by under
+// 1% as long as none waited in the softmax.)
 // The LDS pointers are restrict-qualified: the buffers written by direct-to-LDS loads here are
 // never the ones read here, which lets the compiler drop its own blanket wait on those loads.
 template <bool kWide>
@@ -348,22 +352,22 @@ __device__ __forceinline__ void tile_step(const Ctx& x, int t, int c_begin, cons
                                        bf.kv + ((t + 2) % kBufs) * kTileBytes);
   uint8_t* const meta_dst = bf.meta + ((t + 4) % kMetaStages) * kMetaBytes;
   const int meta_c0 = tile_c0 + 4 * kTile;
-  // load slots: 0-35 follow the score MFMAs, 36-39 the softmax chunks (unused), 40-55 the PV MFMA
-  // pairs
+  // load slots: 0-35 follow the score MFMAs, 36-39 the softmax chunks, 40-55 the PV MFMA pairs;
+  // only PV slots are used (the ring buffer written is free only after the score-exchange barrier)
   auto loads = [&](int slot) {
     switch (slot) {  // slot is a constant after unrolling
-      case 1: kv_gather_group<kWide, 0>(gat); break;
-      case 8: kv_gather_group<kWide, 1>(gat); break;
-      case 15: kv_gather_group<kWide, 2>(gat); break;
-      case 22: kv_gather_group<kWide, 3>(gat); break;
-      case 29: kv_gather_group<kWide, 4>(gat); break;
-      case 33: kv_gather_group<kWide, 5>(gat); break;
-      case 40: kv_gather_group<kWide, 6>(gat); break;
-      case 43: kv_gather_group<kWide, 7>(gat); break;
-      case 47: kv_gather_group<kWide, 8>(gat); break;
+      case 40: kv_gather_group<kWide, 0>(gat); break;
+      case 41: kv_gather_group<kWide, 1>(gat); break;
+      case 42: kv_gather_group<kWide, 2>(gat); break;
+      case 43: kv_gather_group<kWide, 3>(gat); break;
+      case 44: kv_gather_group<kWide, 4>(gat); break;
+      case 45: kv_gather_group<kWide, 5>(gat); break;
+      case 46: kv_gather_group<kWide, 6>(gat); break;
+      case 47: kv_gather_group<kWide, 7>(gat); break;
+      case 48: kv_gather_group<kWide, 8>(gat); break;
       case 49: issue_meta_part<0>(xm, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, meta_c0, meta_dst); break;
-      case 52: issue_meta_part<1>(xm, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, meta_c0, meta_dst); break;
-      case 54: issue_meta_part<2>(xm, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, meta_c0, meta_dst); break;
+      case 51: issue_meta_part<1>(xm, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, meta_c0, meta_dst); break;
+      case 53: issue_meta_part<2>(xm, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, meta_c0, meta_dst); break;
       default: break;
     }
   };
@@ -466,7 +470,9 @@ __device__ __forceinline__ void tile_step(const Ctx& x, int t, int c_begin, cons
   // 4. probability exchange inside the pair
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) *reinterpret_cast<bf16x8*>(bf.p_mine + kk * 1024) = pb_own[kk];
-  lds_barrier();  // every wave's own-block probabilities are in LDS
+  // this wave's row loads of tile t+1 (issued in the previous step's PV phase) have landed; after
+  // the barrier every wave's have, so the next step needs no barrier of its own
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   bf16x8 pb_oth[2];
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) pb_oth[kk] = *reinterpret_cast<const bf16x8*>(bf.p_other + kk * 1024);
@@ -509,8 +515,11 @@ __device__ __forceinline__ void tile_step(const Ctx& x, int t, int c_begin, cons
 //
 // Vector-memory pipeline: everything a tile needs arrives through direct-to-LDS loads, so no loaded
 // register is waited on inside the loop. Step t issues the 9 row loads of tile t+2 and the n_meta
-// metadata loads of tile t+4. Loads retire in order, so "at most 9 + n_meta outstanding" at the top
-// of step t means everything issued up to step t-2 (tile t's rows, tile t+2's metadata) has landed.
+// metadata loads of tile t+4; each wave waits for all of its loads before the probability-exchange
+// barrier of every step, so tile t+1 (and the metadata of tile t+3) are in LDS for everyone after
+// it. Before the first step the prologue has issued tiles 0 and 1 and the metadata of tiles 0-3;
+// loads retire in order, so "at most 9 + n_meta outstanding" then means tile 0 and the metadata of
+// tile 2 have landed, and one barrier publishes them.
 // Prefetches past the split read clamped, valid addresses into buffers that are never read.
 // Inputs of the partial kernels that every split reads.
 struct PartialArgs {
@@ -651,18 +660,17 @@ __device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds
     issue_kv<kWide>(x, kv_pool, meta + kMetaBytes, lds_kv + kTileBytes);
     issue_meta(x, kv_indices, out_cache_loc, custom_mask, c_begin + 3 * kTile, meta + 3 * kMetaBytes);
 
-    for (int t = 0; t < ntiles; ++t) {
-      // at most the loads of step t-1 (9 rows + n_meta metadata) outstanding
-      static_assert(kLoadsPerWave + kMetaExtra + 1 < 16, "vmcnt immediate");
-      if (x.n_meta == 1)
-        __builtin_amdgcn_s_waitcnt((kLoadsPerWave + 1) | (0x7 << 4) | (0xF << 8));
-      else if (x.n_meta == 2)
-        __builtin_amdgcn_s_waitcnt((kLoadsPerWave + 2) | (0x7 << 4) | (0xF << 8));
-      else
-        __builtin_amdgcn_s_waitcnt((kLoadsPerWave + 3) | (0x7 << 4) | (0xF << 8));
-      lds_barrier();  // tile t is in LDS; buffer (t+2)%3 and the exchange slots are free again
+    // tile 0 and the metadata of tile 2 have landed (tile 1 may still be in flight)
+    static_assert(kLoadsPerWave + kMetaExtra + 1 < 16, "vmcnt immediate");
+    if (x.n_meta == 1)
+      __builtin_amdgcn_s_waitcnt((kLoadsPerWave + 1) | (0x7 << 4) | (0xF << 8));
+    else if (x.n_meta == 2)
+      __builtin_amdgcn_s_waitcnt((kLoadsPerWave + 2) | (0x7 << 4) | (0xF << 8));
+    else
+      __builtin_amdgcn_s_waitcnt((kLoadsPerWave + 3) | (0x7 << 4) | (0xF << 8));
+    lds_barrier();
+    for (int t = 0; t < ntiles; ++t)
       tile_step<kWide>(x, t, c_begin, gl, bf, q, oacc, m_ref, l_lane, over, best_raw, best_col);
-    }
     // the last iterations prefetched rows past the split; let them land before LDS is reused
     __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0)
 
