@@ -10,16 +10,18 @@
 //                          tiles), shared by all 128 query rows (2 wave pairs x 64 rows). QK^T and
 //                          PV run on 32x32x16 bf16 MFMA with fp32 accumulation; the mask lookup
 //                          and online softmax happen in registers between the two.
-//   verify_combine_kernel  one workgroup per query row: log-sum-exp combine of the row's partials
-//                          into the bf16 output and the fp32 natural-log LSE.
+//   verify_combine_kernel  log-sum-exp combine of each query row's partials into the bf16 output
+//                          and the fp32 natural-log LSE (one, four or, below 512 rows, a quarter
+//                          row per workgroup).
 //
 // Layout conventions of the partial kernel (per MFMA block of 32 query rows r, columns c of one
 // tile):
 //   S^T[c][r] = K[c][:] . Q[r][:]  (A = K from LDS, B = Q resident in VGPRs)
 //   O^T[e][r] += V^T[e][c] . P^T[c][r]  (A = V^T via ds_read_b64_tr_b16, B = P^T from registers)
 // so each lane holds one query row (lane % 32) for both S^T and O^T, and the softmax statistics
-// never leave the lane (only the lane pair l, l^32 shares a row). A wave keeps two such blocks, so
-// every K or V fragment it reads from LDS feeds two MFMAs.
+// never leave the lane (only the lane pair l, l^32 shares a row). A wave scores one such block
+// over the whole row and accumulates the output of two (its own and its partner's) over half the
+// output columns, so every V fragment it reads from LDS feeds two MFMAs.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -52,7 +54,6 @@ constexpr int kRowsPerLoader = kTile / kLoaders;         // 8
 constexpr int kLoadsPerWave = kRowsPerLoader * kChunks / 64;  // 9 direct-to-LDS loads
 constexpr int kHalfSteps = (kLatent + kRope) / 32;       // 18 k-steps of 16 per half of the row
 constexpr int kHalfEBlocks = kLatent / 64;               // 8 blocks of 32 output columns per half
-constexpr int kSXchgBytes = 64 * 16 * 4;                 // one 32x32 block of fp32 partial scores
 constexpr int kPXchgBytes = 64 * 16 * 2;                 // one 32x32 block of bf16 probabilities
 constexpr float kHeadroom = 64.0f;  // scores may exceed a row's reference max by this (log2 units)
 // Per-tile metadata of one wave, all through byte-granular direct-to-LDS loads (each byte lands
@@ -64,7 +65,7 @@ constexpr int kMetaExtra = 2;                    // extra mask loads at most (bl
 constexpr int kMetaTokens = 1 + 2 * kMetaExtra;  // block tokens whose mask bytes ride in LDS
 constexpr int kMetaBytes = 256 * (1 + kMetaExtra);
 constexpr int kMetaStages = 8;                   // per-wave ring of per-tile metadata
-constexpr int kLdsBytes = kBufs * kTileBytes + kWaves * (kSXchgBytes + kPXchgBytes + kMetaStages * kMetaBytes);
+constexpr int kLdsBytes = kBufs * kTileBytes + kWaves * (2 * kPXchgBytes + kMetaStages * kMetaBytes);
 
 static_assert(kRowsPerLoader * kChunks % 64 == 0, "loader must tile whole wave instructions");
 static_assert(kWaves == kLoaders, "every wave gathers a share of each tile");
@@ -287,37 +288,36 @@ struct Glob {
 };
 
 // LDS areas of one wave: the shared tile ring, its private metadata ring, and its lane's entries in
-// the score and probability exchange slots.
+// the two probability exchange slots (step parity) of its own and its partner's.
 struct Bufs {
   uint8_t* kv;
   uint8_t* meta;
-  uint8_t* s_mine;
-  const uint8_t* s_other;
   uint8_t* p_mine;
   const uint8_t* p_other;
 };
 
-// One 32-column tile for one wave. Register set 0 of the wave (q[0], oacc[0]) is its own row block
-// (rows 32hf .. 32hf+31 of the pair), set 1 the partner's block; both hold this wave's half hf of
-// the 576-wide query row and of the 512-wide output row.
-//   1. partial scores of both blocks over the half: each K fragment is read from LDS once and feeds
-//      two MFMAs
-//   2. the partner block's partial goes to LDS; after the barrier the partner's partial of the own
-//      block is added (each wave completes the scores of one block)
-//   3. mask + softmax numerators of the own block against its fixed reference max
-//   4. the bf16 probabilities of the own block go to LDS; after the barrier the partner's are read
-//   5. O^T of both blocks over the output half: each V fragment is read once and feeds two MFMAs
-// Two barriers per step, and they also order the tile ring, so a step needs none of its own:
-//  - the score-exchange barrier of step t comes after every wave's PV of step t-1, so ring buffer
-//    (t+2) % 3, which held tile t-1, is free once it has passed;
-//  - before the probability-exchange barrier each wave waits for all its loads (vmcnt(0)): the row
-//    loads of tile t+1 it issued in step t-1; after that barrier tile t+1 is whole in LDS for every
-//    wave, ready for step t+1.
+// One 32-column tile for one wave. The wave holds the whole 576-wide query row of its own block
+// (rows 32hf .. 32hf+31 of the pair; q) and its half hf of the 512-wide output row of both blocks
+// of the pair (oacc[0] own, oacc[1] the partner's).
+//   1. scores of the own block over the whole row: 36 MFMAs, one per K fragment
+//   2. mask + softmax numerators of the own block against its fixed reference max
+//   3. the bf16 probabilities go to LDS (slot t % 2); after the barrier the partner's are read
+//   4. O^T of both blocks over the output half: each V fragment is read once and feeds two MFMAs
+// One barrier per step, and it also orders the tile ring:
+//  - it comes after every wave's PV of step t-1, so ring buffer (t+2) % 3, which held tile t-1, is
+//    free once it has passed;
+//  - before it each wave waits for all its loads (vmcnt(0)): the row loads of tile t+1 it issued in
+//    step t-1; after it tile t+1 is whole in LDS for every wave, ready for step t+1;
+//  - the probability slots alternate with the step, so a wave writing step t+1's probabilities
+//    cannot overwrite step t's before its partner has read them (it read them before arriving at
+//    the barrier of step t+1).
 // Hence the step issues the 9 row loads of tile t+2 and the metadata loads of tile t+4 in the PV
-// phase, between the MFMAs, after the probability-exchange barrier; a load has about one step to
-// land. (With a third barrier opening each step and the loads spread over the score and PV phases,
-// the step was 4% slower at the 185k batch; where the loads sit inside the step moved it by under
-// 1% as long as none waited in the softmax.)
+// phase, between the MFMAs, after the barrier; a load has about one step to land. History at the
+// 185k batch: three barriers per step (one opening the step, one exchanging the two waves' partial
+// scores over their row halves, one for the probabilities) 800 us; without the opening one 767 us;
+// with each wave scoring its own block over the whole row, so no score exchange, 707 us, although
+// every K fragment then feeds one MFMA instead of two (36.8 KB of K reads per wave and tile instead
+// of 18.4 KB). Where the loads sit inside the PV phase moves the step by under 1%.
 // The LDS pointers are restrict-qualified: the buffers written by direct-to-LDS loads here are
 // never the ones read here, which lets the compiler drop its own blanket wait on those loads.
 template <bool kWide>
@@ -334,13 +334,13 @@ __device__ __forceinline__ void tile_step(const Ctx& x, int t, int c_begin, cons
   const uint8_t* __restrict__ kb = bf.kv + (t % kBufs) * kTileBytes;
   // LDS offsets of this lane's K and V fragments, rebuilt each step from the opaque lane (cheaper
   // than keeping six more registers live across the loop). K: the lane reads logical chunk
-  // 36hf + 2ks + g of tile row (lane & 31). V (transposed reads): the 16-lane group G reads tile rows
+  // 2ks + g of tile row (lane & 31). V (transposed reads): the 16-lane group G reads tile rows
   // 16kk + 8m + 4(G/2) + (k16/4), m = 0, 1, latent columns 32eb + 16(G%2) + 4(k16%4) .. +3 of block
   // eb = 8hf + leb, i.e. logical chunk 4eb + vc with vc = 2(G%2) + (k16%4)/2; the hf part is folded
   // into the offsets.
   int k_off[4], v_off0, v_off1;
 #pragma unroll
-  for (int b4 = 0; b4 < 4; ++b4) k_off[b4] = tile_offset(xm.lane & 31, 36 * x.hf + 2 * b4 + xm.g);
+  for (int b4 = 0; b4 < 4; ++b4) k_off[b4] = tile_offset(xm.lane & 31, 2 * b4 + xm.g);
   {
     const int k16 = xm.lane & 15, G = xm.lane >> 4;
     const int v_row = 4 * (G >> 1) + (k16 >> 2);
@@ -372,13 +372,14 @@ __device__ __forceinline__ void tile_step(const Ctx& x, int t, int c_begin, cons
     }
   };
 
-  // 1. S^T = K[:, half] . Q[:, half]^T for the own block (s_own) and the partner's (s_give), one
-  // k-step at a time; fragment ks is logical chunk 36hf + 2ks + g of row (lane & 31), at
-  // k_off[ks % 4] + 1024 (ks / 4), read kKAhead k-steps ahead.
-  f32x16 s_own = {}, s_give = {};
+  // 1. S^T = K . Q^T for the own block (s_own), one k-step at a time; fragment ks is logical chunk
+  // 2ks + g of row (lane & 31), at k_off[ks % 4] + 1024 (ks / 4), read kKAhead k-steps ahead; query
+  // k-step ks is q[ks / 18][ks % 18].
+  f32x16 s_own = {};
   uint32_t bits;
   {
     constexpr int kKAhead = 2;
+    constexpr int kSteps = 2 * kHalfSteps;  // 36 k-steps over the whole 576-wide row
     bf16x8 kf[kKAhead + 1];
     auto load_k = [&](int ks) {
       kf[ks % (kKAhead + 1)] = *reinterpret_cast<const bf16x8*>(kb + k_off[ks % 4] + kGroupBytes * (ks / 4));
@@ -386,31 +387,16 @@ __device__ __forceinline__ void tile_step(const Ctx& x, int t, int c_begin, cons
 #pragma unroll
     for (int ks = 0; ks < kKAhead; ++ks) load_k(ks);
 #pragma unroll
-    for (int ks = 0; ks < kHalfSteps; ++ks) {
-      if (ks + kKAhead < kHalfSteps) load_k(ks + kKAhead);
+    for (int ks = 0; ks < kSteps; ++ks) {
+      if (ks + kKAhead < kSteps) load_k(ks + kKAhead);
       __builtin_amdgcn_sched_barrier(0);
-      s_own = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks % (kKAhead + 1)], q[0][ks], s_own, 0, 0, 0);
+      s_own = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks % (kKAhead + 1)], q[ks / kHalfSteps][ks % kHalfSteps],
+                                                      s_own, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      loads(2 * ks);
-      __builtin_amdgcn_sched_barrier(0);
-      s_give = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks % (kKAhead + 1)], q[1][ks], s_give, 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      loads(2 * ks + 1);
+      loads(ks);
       __builtin_amdgcn_sched_barrier(0);
     }
     bits = mask_word(xm, gl.custom_mask, bf.meta + (t % kMetaStages) * kMetaBytes, tile_c0);
-  }
-
-  // 2. score exchange inside the pair
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-    *reinterpret_cast<f32x4*>(bf.s_mine + k * 1024) = f32x4{s_give[4 * k], s_give[4 * k + 1], s_give[4 * k + 2], s_give[4 * k + 3]};
-  lds_barrier();  // every wave's partner-block partial is in LDS
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const f32x4 o = *reinterpret_cast<const f32x4*>(bf.s_other + k * 1024);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) s_own[4 * k + j] += o[j];
   }
   loads(36);
 
@@ -469,13 +455,14 @@ __device__ __forceinline__ void tile_step(const Ctx& x, int t, int c_begin, cons
 
   // 4. probability exchange inside the pair
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) *reinterpret_cast<bf16x8*>(bf.p_mine + kk * 1024) = pb_own[kk];
+  for (int kk = 0; kk < 2; ++kk) *reinterpret_cast<bf16x8*>(bf.p_mine + (t & 1) * kPXchgBytes + kk * 1024) = pb_own[kk];
   // this wave's row loads of tile t+1 (issued in the previous step's PV phase) have landed; after
   // the barrier every wave's have, so the next step needs no barrier of its own
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   bf16x8 pb_oth[2];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) pb_oth[kk] = *reinterpret_cast<const bf16x8*>(bf.p_other + kk * 1024);
+  for (int kk = 0; kk < 2; ++kk)
+    pb_oth[kk] = *reinterpret_cast<const bf16x8*>(bf.p_other + (t & 1) * kPXchgBytes + kk * 1024);
 
   // 5. O^T[e half] += V^T . P^T for both blocks; k-step kk covers tile columns [16kk, 16kk+16)
   // permuted as logical k = 8g + j  <->  column 16kk + 4g + j (j < 4), 16kk + 8 + 4g + (j - 4)
@@ -507,10 +494,9 @@ __device__ __forceinline__ void tile_step(const Ctx& x, int t, int c_begin, cons
   }
 }
 
-// Partial kernel. Wave pair p owns 64 query rows in two blocks of 32; its wave h (0/1) holds, for
-// both blocks, the query values of the row half d in [288h, 288h + 288) and the output columns
-// e in [256h, 256h + 256), and runs the softmax of block h. Per 32-column tile each wave computes
-// the partial scores of both blocks over its half, the pair swaps the partials and then the
+// Partial kernel. Wave pair p owns 64 query rows in two blocks of 32; its wave h (0/1) holds the
+// whole query rows of block h and, for both blocks, the output columns e in [256h, 256h + 256).
+// Per 32-column tile each wave scores and softmaxes its own block, the pair swaps the bf16
 // probabilities through LDS, and each wave updates its output half of both blocks.
 //
 // Vector-memory pipeline: everything a tile needs arrives through direct-to-LDS loads, so no loaded
@@ -542,7 +528,6 @@ struct PartialArgs {
 // The partial kernels' LDS.
 struct PartialLds {
   uint8_t* kv;
-  uint8_t* s;
   uint8_t* p;
   uint8_t* meta;
   int* over;
@@ -584,17 +569,16 @@ __device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds
   // ---- this wave's half of both blocks' query rows as MFMA B operands: k-step ks of set i holds
   // Q[row][288 hf + 16 ks + 8 g .. +8] (rows past R load row R-1 and are zeroed)
   bf16x8 q[2][kHalfSteps];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = set_row(i);
+  {
+    const int row = own_row;
     const int q_row = min(row, R - 1);
     const bf16x8* qn = reinterpret_cast<const bf16x8*>(q_nope + ((size_t)b * R + q_row) * kLatent);
     const bf16x8* qr = reinterpret_cast<const bf16x8*>(q_rope + ((size_t)b * R + q_row) * kRope);
 #pragma unroll
-    for (int ks = 0; ks < kHalfSteps; ++ks) {
-      const int chunk8 = 36 * hf + 2 * ks + g;  // 8-value chunk of the 576-wide row
+    for (int ks = 0; ks < 2 * kHalfSteps; ++ks) {
+      const int chunk8 = 2 * ks + g;  // 8-value chunk of the 576-wide row
       const bf16x8 v = chunk8 < kLatent / 8 ? qn[chunk8] : qr[chunk8 - kLatent / 8];
-      q[i][ks] = row < R ? v : bf16x8{};
+      q[ks / kHalfSteps][ks % kHalfSteps] = row < R ? v : bf16x8{};
     }
   }
 
@@ -623,9 +607,8 @@ __device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds
   x.scale_log2 = a.scale_log2;
   uint8_t* const meta = lds.meta + w * kMetaStages * kMetaBytes;
   uint8_t* const lds_kv = lds.kv;
-  const Bufs bf = {lds_kv, meta,
-                   lds.s + w * kSXchgBytes + lane * 16, lds.s + (w ^ 1) * kSXchgBytes + lane * 16,
-                   lds.p + w * kPXchgBytes + lane * 16, lds.p + (w ^ 1) * kPXchgBytes + lane * 16};
+  const Bufs bf = {lds_kv, meta, lds.p + w * 2 * kPXchgBytes + lane * 16,
+                   lds.p + (w ^ 1) * 2 * kPXchgBytes + lane * 16};
   const Glob gl = {kv_pool, kv_indices, out_cache_loc, custom_mask};
 
   const int ntiles = (c_end - c_begin + kTile - 1) / kTile;
@@ -736,11 +719,10 @@ __device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds
 
 #define PARTIAL_LDS_DECL                                                          \
   __shared__ __attribute__((aligned(16))) uint8_t lds_kv[kBufs * kTileBytes];     \
-  __shared__ __attribute__((aligned(16))) uint8_t lds_s[kWaves * kSXchgBytes];    \
-  __shared__ __attribute__((aligned(16))) uint8_t lds_p[kWaves * kPXchgBytes];    \
+  __shared__ __attribute__((aligned(16))) uint8_t lds_p[kWaves * 2 * kPXchgBytes];\
   __shared__ __attribute__((aligned(16))) uint8_t lds_meta[kWaves * kMetaStages * kMetaBytes]; \
   __shared__ int lds_over[kWaves];                                                \
-  const PartialLds lds = {lds_kv, lds_s, lds_p, lds_meta, lds_over};
+  const PartialLds lds = {lds_kv, lds_p, lds_meta, lds_over};
 
 // Per-request splits: workgroup -> (request b, split s, row tile) by decode_unit; split s of request
 // b covers columns [s*chunk, min(L_b, (s+1)*chunk)) with chunk = ceil(L_b / nsplit) rounded up to the
