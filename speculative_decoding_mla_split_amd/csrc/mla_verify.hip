@@ -378,7 +378,7 @@ __device__ __forceinline__ void tile_step(const Ctx& x, int t, int c_begin, cons
   f32x16 s_own = {};
   uint32_t bits;
   {
-    constexpr int kKAhead = 2;
+    constexpr int kKAhead = 3;
     constexpr int kSteps = 2 * kHalfSteps;  // 36 k-steps over the whole 576-wide row
     bf16x8 kf[kKAhead + 1];
     auto load_k = [&](int ks) {
