@@ -312,12 +312,9 @@ struct Bufs {
 //    cannot overwrite step t's before its partner has read them (it read them before arriving at
 //    the barrier of step t+1).
 // Hence the step issues the 9 row loads of tile t+2 and the metadata loads of tile t+4 in the PV
-// phase, between the MFMAs, after the barrier; a load has about one step to land. History at the
-// 185k batch: three barriers per step (one opening the step, one exchanging the two waves' partial
-// scores over their row halves, one for the probabilities) 800 us; without the opening one 767 us;
-// with each wave scoring its own block over the whole row, so no score exchange, 707 us, although
-// every K fragment then feeds one MFMA instead of two (36.8 KB of K reads per wave and tile instead
-// of 18.4 KB). Where the loads sit inside the PV phase moves the step by under 1%.
+// phase, between the MFMAs, after the barrier; a load has about one step to land. Scoring the own
+// block over the whole row makes every K fragment feed one MFMA (36.8 KB of K reads per wave and
+// tile), but needs no exchange of partial scores and so no second barrier, which costs more.
 // The LDS pointers are restrict-qualified: the buffers written by direct-to-LDS loads here are
 // never the ones read here, which lets the compiler drop its own blanket wait on those loads.
 template <bool kWide>
@@ -352,22 +349,22 @@ __device__ __forceinline__ void tile_step(const Ctx& x, int t, int c_begin, cons
                                        bf.kv + ((t + 2) % kBufs) * kTileBytes);
   uint8_t* const meta_dst = bf.meta + ((t + 4) % kMetaStages) * kMetaBytes;
   const int meta_c0 = tile_c0 + 4 * kTile;
-  // load slots: 0-35 follow the score MFMAs, 36-39 the softmax chunks, 40-55 the PV MFMA pairs;
-  // only PV slots are used (the ring buffer written is free only after the score-exchange barrier)
-  auto loads = [&](int slot) {
-    switch (slot) {  // slot is a constant after unrolling
-      case 40: kv_gather_group<kWide, 0>(gat); break;
-      case 41: kv_gather_group<kWide, 1>(gat); break;
-      case 42: kv_gather_group<kWide, 2>(gat); break;
-      case 43: kv_gather_group<kWide, 3>(gat); break;
-      case 44: kv_gather_group<kWide, 4>(gat); break;
-      case 45: kv_gather_group<kWide, 5>(gat); break;
-      case 46: kv_gather_group<kWide, 6>(gat); break;
-      case 47: kv_gather_group<kWide, 7>(gat); break;
-      case 48: kv_gather_group<kWide, 8>(gat); break;
-      case 49: issue_meta_part<0>(xm, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, meta_c0, meta_dst); break;
-      case 51: issue_meta_part<1>(xm, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, meta_c0, meta_dst); break;
-      case 53: issue_meta_part<2>(xm, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, meta_c0, meta_dst); break;
+  // the loads of the step, one after each PV MFMA pair f (the ring buffer they fill is free only
+  // after the step's barrier)
+  auto loads = [&](int f) {
+    switch (f) {  // f is a constant after unrolling
+      case 0: kv_gather_group<kWide, 0>(gat); break;
+      case 1: kv_gather_group<kWide, 1>(gat); break;
+      case 2: kv_gather_group<kWide, 2>(gat); break;
+      case 3: kv_gather_group<kWide, 3>(gat); break;
+      case 4: kv_gather_group<kWide, 4>(gat); break;
+      case 5: kv_gather_group<kWide, 5>(gat); break;
+      case 6: kv_gather_group<kWide, 6>(gat); break;
+      case 7: kv_gather_group<kWide, 7>(gat); break;
+      case 8: kv_gather_group<kWide, 8>(gat); break;
+      case 9: issue_meta_part<0>(xm, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, meta_c0, meta_dst); break;
+      case 11: issue_meta_part<1>(xm, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, meta_c0, meta_dst); break;
+      case 13: issue_meta_part<2>(xm, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, meta_c0, meta_dst); break;
       default: break;
     }
   };
@@ -393,14 +390,11 @@ __device__ __forceinline__ void tile_step(const Ctx& x, int t, int c_begin, cons
       s_own = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks % (kKAhead + 1)], q[ks / kHalfSteps][ks % kHalfSteps],
                                                       s_own, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      loads(ks);
-      __builtin_amdgcn_sched_barrier(0);
     }
     bits = mask_word(xm, gl.custom_mask, bf.meta + (t % kMetaStages) * kMetaBytes, tile_c0);
   }
-  loads(36);
 
-  // 3. mask + softmax numerators against the row's reference max m_ref (base-2 units of the scaled
+  // 2. mask + softmax numerators against the row's reference max m_ref (base-2 units of the scaled
   // score). The reference is the max of the first tile with a visible column and then stays fixed,
   // so the accumulators are never rescaled; a later score above m_ref + kHeadroom raises `over`,
   // and the kernel then reruns the split with m_ref = the row's true max. Element i of s_own is
@@ -434,7 +428,6 @@ __device__ __forceinline__ void tile_step(const Ctx& x, int t, int c_begin, cons
   m_ref = m_ref == -INFINITY ? mx : m_ref;
   over = over || mx > m_ref + kHeadroom;
   const float base = m_ref == -INFINITY ? 0.0f : m_ref;
-  loads(37);
   bf16x8 pb_own[2];
   float psum = 0.0f;
 #pragma unroll
@@ -445,15 +438,10 @@ __device__ __forceinline__ void tile_step(const Ctx& x, int t, int c_begin, cons
     psum += p0 + p1;
     pb_own[i >> 3][i & 7] = pk[0];
     pb_own[i >> 3][(i & 7) + 1] = pk[1];
-    if (i == 6) {
-      __builtin_amdgcn_sched_barrier(0);
-      loads(38);
-      __builtin_amdgcn_sched_barrier(0);
-    }
   }
   l_lane += psum;
 
-  // 4. probability exchange inside the pair
+  // 3. probability exchange inside the pair
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) *reinterpret_cast<bf16x8*>(bf.p_mine + (t & 1) * kPXchgBytes + kk * 1024) = pb_own[kk];
   // this wave's row loads of tile t+1 (issued in the previous step's PV phase) have landed; after
@@ -464,7 +452,7 @@ __device__ __forceinline__ void tile_step(const Ctx& x, int t, int c_begin, cons
   for (int kk = 0; kk < 2; ++kk)
     pb_oth[kk] = *reinterpret_cast<const bf16x8*>(bf.p_other + (t & 1) * kPXchgBytes + kk * 1024);
 
-  // 5. O^T[e half] += V^T . P^T for both blocks; k-step kk covers tile columns [16kk, 16kk+16)
+  // 4. O^T[e half] += V^T . P^T for both blocks; k-step kk covers tile columns [16kk, 16kk+16)
   // permuted as logical k = 8g + j  <->  column 16kk + 4g + j (j < 4), 16kk + 8 + 4g + (j - 4)
   // (j >= 4). V fragment f = (kk, leb) = (f / 8, f % 8) is read kVAhead fragments ahead with two
   // transposed reads and feeds the MFMAs of both blocks.
@@ -489,7 +477,7 @@ __device__ __forceinline__ void tile_step(const Ctx& x, int t, int c_begin, cons
     __builtin_amdgcn_sched_barrier(0);
     oacc[1][leb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[f % (kVAhead + 1)], pb_oth[kk], oacc[1][leb], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
-    loads(40 + f);
+    loads(f);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
