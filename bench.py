@@ -95,7 +95,7 @@ class Workload:
     def combine(self, stream):
         inp = self.inp
         call = self.pkg.balanced_combine_raw if self.balanced else self.pkg.combine_raw
-        rc = call(self.ws.data_ptr(), self.ws_bytes, inp.B, inp.q_len, inp.H, self.nsplit,
+        rc = call(self.ws.data_ptr(), self.ws_bytes, self.pool.data_ptr(), inp.N, inp.B, inp.q_len, inp.H, self.nsplit,
                   self.out.data_ptr(), self.lse.data_ptr(), stream.cuda_stream)
         assert rc == 0, self.pkg.status_string(rc)
 

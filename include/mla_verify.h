@@ -66,7 +66,7 @@ typedef enum {
  * Ceiling", "The Architecture of Capture Safety": the workspace is allocated once, outside
  * the step). It holds one partial per (request, split, draft token, head): the running max
  * and sum (2 floats), the unnormalised 512-wide accumulator (512 floats) and the top record
- * (16 bytes).
+ * (8 bytes).
  * Returns 0 when an argument is out of range (B, q_len, H < 1; nsplit outside [1, 1024]).
  */
 size_t mla_verify_attn_workspace_size(int B, int q_len, int H, int nsplit);
@@ -131,16 +131,16 @@ int mla_verify_attn(const void *q_nope, const void *q_rope, const void *kv_pool,
  * split), its sum l of 2^(score*log2(e) - m), its unnormalised 512-wide accumulator (every
  * probability rounded to bf16 before it multiplies a value row, as the matrix cores take it) and
  * its top record: the exact probability p of the split's largest visible score (same base as l)
- * and the device address of that column's 576-wide pool row. Laid out as
+ * and the pool slot (already clamped into [0, N)) of that column's 576-wide row. Laid out as
  * float2 ml[B][nsplit][q_len*H], then float acc[B][nsplit][q_len*H][512], then
- * int32x4 top[B][nsplit][q_len*H] = {bits of p, address low 32 bits, address high 32 bits, 0},
- * each region starting at a 256-byte boundary. The combine adds w_s (p - bf16(p)) times the first
- * 512 values of that row for every split whose p w_s is at least 1/32 of the row's final sum
- * (exact probability restored for the columns that dominate a row); it reads the pool rows
- * through the recorded addresses, so the pool must still be valid when it runs. A caller may
- * move these partials between the two calls (for example to combine partials computed for
- * different column ranges elsewhere); the combine needs only this layout. Calls with the same
- * (B, q_len, H, nsplit) must be used for both.
+ * int32x2 top[B][nsplit][q_len*H] = {bits of p, slot}, each region starting at a 256-byte
+ * boundary. The combine adds w_s (p - bf16(p)) times the first 512 values of pool row `slot`
+ * for every split whose p w_s is at least 1/32 of the row's final sum (exact probability restored
+ * for the columns that dominate a row). It reads those rows from `kv_pool` (clamping the slot into
+ * [0, N) again, so no read leaves the pool whatever the workspace holds); kv_pool and N must be
+ * the ones the partial call used, and its rows must be unchanged in between. A caller may move the
+ * partials to another buffer or device between the two calls as long as the combine is given the
+ * same pool contents. Calls with the same (B, q_len, H, nsplit) must be used for both.
  */
 int mla_verify_attn_partial(const void *q_nope, const void *q_rope, const void *kv_pool, int64_t N,
                             const int32_t *kv_indptr, const int32_t *kv_indices,
@@ -149,8 +149,9 @@ int mla_verify_attn_partial(const void *q_nope, const void *q_rope, const void *
                             int nsplit, void *workspace, size_t workspace_bytes,
                             hipStream_t stream);
 
-int mla_verify_attn_combine(const void *workspace, size_t workspace_bytes, int B, int q_len, int H,
-                            int nsplit, void *out, float *lse, hipStream_t stream);
+int mla_verify_attn_combine(const void *workspace, size_t workspace_bytes, const void *kv_pool,
+                            int64_t N, int B, int q_len, int H, int nsplit, void *out, float *lse,
+                            hipStream_t stream);
 
 /*
  * Balanced partition of the same computation. The per-request splits above give every request
@@ -176,7 +177,7 @@ int mla_verify_attn_combine(const void *workspace, size_t workspace_bytes, int B
  *
  * The workspace holds the plan (split_info int32x4 [units]: {request, first column, end column, 0}
  * of each split, {-1, 0, 0, 0} if unused; then split_start int32 [B + 1]: the running sum of n_b),
- * then float2 ml [units][q_len*H], float acc [units][q_len*H][512] and int32x4 top
+ * then float2 ml [units][q_len*H], float acc [units][q_len*H][512] and int32x2 top
  * [units][q_len*H] partials as described for mla_verify_attn_partial (split split_start[b] + s of
  * request b at block split_start[b] + s), each region 256-byte aligned.
  * mla_verify_attn_balanced_partial writes the plan and the partials (for B <= 64 the partial
@@ -200,8 +201,9 @@ int mla_verify_attn_balanced_partial(const void *q_nope, const void *q_rope, con
                                      int units, void *workspace, size_t workspace_bytes,
                                      hipStream_t stream);
 
-int mla_verify_attn_balanced_combine(const void *workspace, size_t workspace_bytes, int B, int q_len,
-                                     int H, int units, void *out, float *lse, hipStream_t stream);
+int mla_verify_attn_balanced_combine(const void *workspace, size_t workspace_bytes, const void *kv_pool,
+                                     int64_t N, int B, int q_len, int H, int units, void *out, float *lse,
+                                     hipStream_t stream);
 
 #ifdef __cplusplus
 }

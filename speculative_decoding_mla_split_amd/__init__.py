@@ -45,7 +45,7 @@ def library() -> ctypes.CDLL:
         lib.mla_verify_attn_partial.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, vp, i32, i32, i32, f32, i32, vp,
                                                 sz, vp]
         lib.mla_verify_attn_partial.restype = i32
-        lib.mla_verify_attn_combine.argtypes = [vp, sz, i32, i32, i32, i32, vp, vp, vp]
+        lib.mla_verify_attn_combine.argtypes = [vp, sz, vp, i64, i32, i32, i32, i32, vp, vp, vp]
         lib.mla_verify_attn_combine.restype = i32
         lib.mla_verify_attn_balanced_workspace_size.argtypes = [i32, i32, i32, i32]
         lib.mla_verify_attn_balanced_workspace_size.restype = sz
@@ -97,10 +97,10 @@ def partial_raw(q_nope, q_rope, kv_pool, N, kv_indptr, kv_indices, out_cache_loc
                                                  float(scale), int(nsplit), workspace, int(workspace_bytes), stream))
 
 
-def combine_raw(workspace, workspace_bytes, B, q_len, H, nsplit, out, lse, stream) -> int:
+def combine_raw(workspace, workspace_bytes, kv_pool, N, B, q_len, H, nsplit, out, lse, stream) -> int:
     """Direct call of mla_verify_attn_combine with integer device addresses; returns the status."""
-    return int(library().mla_verify_attn_combine(workspace, int(workspace_bytes), int(B), int(q_len), int(H),
-                                                 int(nsplit), out, lse, stream))
+    return int(library().mla_verify_attn_combine(workspace, int(workspace_bytes), kv_pool, int(N), int(B), int(q_len),
+                                                 int(H), int(nsplit), out, lse, stream))
 
 
 def balanced_workspace_size(B: int, q_len: int, H: int, units: int) -> int:
@@ -126,10 +126,10 @@ def balanced_partial_raw(q_nope, q_rope, kv_pool, N, kv_indptr, kv_indices, out_
                                                           int(workspace_bytes), stream))
 
 
-def balanced_combine_raw(workspace, workspace_bytes, B, q_len, H, units, out, lse, stream) -> int:
+def balanced_combine_raw(workspace, workspace_bytes, kv_pool, N, B, q_len, H, units, out, lse, stream) -> int:
     """Direct call of mla_verify_attn_balanced_combine; returns the status."""
-    return int(library().mla_verify_attn_balanced_combine(workspace, int(workspace_bytes), int(B), int(q_len),
-                                                          int(H), int(units), out, lse, stream))
+    return int(library().mla_verify_attn_balanced_combine(workspace, int(workspace_bytes), kv_pool, int(N), int(B),
+                                                          int(q_len), int(H), int(units), out, lse, stream))
 
 
 REPORT_MAX_OUT, REPORT_MAX_LSE, REPORT_ROWS, REPORT_BAD, REPORT_WORDS = 0, 1, 2, 3, 4

@@ -510,7 +510,7 @@ struct PartialArgs {
   float scale_log2;
   float2* ws_ml;
   float* ws_acc;
-  int4* ws_top;
+  int2* ws_top;
 };
 
 // The partial kernels' LDS.
@@ -659,8 +659,8 @@ __device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds
 
   // ---- the row's top probability. Each visible column entered the PV product with its probability
   // rounded to bf16 (the sum l took the exact values). For the row's largest one (the same fma +
-  // exp2 as in the tile, so the same value) the exact probability and the address of its value row
-  // go to the top record; the combine adds back what the rounding dropped, (p - bf16(p)) times that
+  // exp2 as in the tile, so the same value) the exact probability and the pool slot of its value
+  // row go to the top record; the combine adds back what the rounding dropped, (p - bf16(p)) times that
   // value row, where the column matters against the row's final sum. Without that, a row dominated
   // by one column whose score came after the reference tile is off by up to 2^-9 of that column's
   // values. The lane pair first agrees on the row's best column.
@@ -678,9 +678,7 @@ __device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds
       const float p = top == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(__builtin_fmaf(top, x.scale_log2, -base));
       int slot = col < P ? kv_indices[kv_start + col] : out_cache_loc[(size_t)b * q_len + (col - P)];
       slot = min(max(slot, 0), a.N - 1);
-      const uint64_t vrow = reinterpret_cast<uint64_t>(kv_pool + (size_t)slot * kRowBytes);
-      a.ws_top[part + own_row] =
-          make_int4(__float_as_int(p), (int)(uint32_t)vrow, (int)(uint32_t)(vrow >> 32), 0);
+      a.ws_top[part + own_row] = make_int2(__float_as_int(p), slot);
     }
   }
 
@@ -724,7 +722,7 @@ verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restric
                       const uint8_t* __restrict__ custom_mask,
                       const int32_t* __restrict__ mask_indptr, int B, int q_len, int H,
                       float scale_log2, int nsplit, int n_rt, float2* __restrict__ ws_ml,
-                      float* __restrict__ ws_acc, int4* __restrict__ ws_top) {
+                      float* __restrict__ ws_acc, int2* __restrict__ ws_top) {
   PARTIAL_LDS_DECL
   const PartialArgs a = {q_nope, q_rope, kv_pool, N, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
                          B, q_len, H, scale_log2, ws_ml, ws_acc, ws_top};
@@ -923,7 +921,7 @@ verify_partial_balanced_kernel(const __bf16* __restrict__ q_nope, const __bf16* 
                                const int32_t* __restrict__ mask_indptr, int B, int q_len, int H,
                                float scale_log2, int units, int n_rt, int fused_plan, int4* __restrict__ split_info,
                                int* __restrict__ split_start, float2* __restrict__ ws_ml,
-                               float* __restrict__ ws_acc, int4* __restrict__ ws_top) {
+                               float* __restrict__ ws_acc, int2* __restrict__ ws_top) {
   PARTIAL_LDS_DECL
   const PartialArgs a = {q_nope, q_rope, kv_pool, N, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
                          B, q_len, H, scale_log2, ws_ml, ws_acc, ws_top};
@@ -976,7 +974,7 @@ constexpr int combine_block_waves() { return kWaves == 1 ? 4 : kWaves; }
 template <bool kBalanced, int kWaves>
 __global__ void __launch_bounds__(combine_block_waves<kWaves>() * 64)
 verify_combine_kernel(const float2* __restrict__ ws_ml, const float* __restrict__ ws_acc,
-                      const int4* __restrict__ ws_top, int B, int R,
+                      const int2* __restrict__ ws_top, const uint8_t* __restrict__ kv_pool, int N, int B, int R,
                       int nsplit_or_units, const int* __restrict__ split_start, __bf16* __restrict__ out,
                       float* __restrict__ lse) {
   constexpr int kRed = kWaves > 1 ? kWaves : 2;
@@ -998,11 +996,11 @@ verify_combine_kernel(const float2* __restrict__ ws_ml, const float* __restrict_
     first = (size_t)b * nsplit;
   }
   const float2* ml = ws_ml + first * R + r;
-  const int4* top = ws_top + first * R + r;
+  const int2* top = ws_top + first * R + r;
   // 1. split w*64 + lane: (m, l) and top record in registers; the max over every split
   const int s_own = w * 64 + lane;
   const float2 st_own = s_own < nsplit ? ml[(size_t)s_own * R] : make_float2(-INFINITY, 0.0f);
-  const int4 top_own = s_own < nsplit ? top[(size_t)s_own * R] : make_int4(0, 0, 0, 0);
+  const int2 top_own = s_own < nsplit ? top[(size_t)s_own * R] : make_int2(0, 0);
   float M = st_own.x;
   for (int s = s_own + kWaves * 64; s < nsplit; s += kWaves * 64) M = fmaxf(M, ml[(size_t)s * R].x);
 #pragma unroll
@@ -1060,7 +1058,7 @@ verify_combine_kernel(const float2* __restrict__ ws_ml, const float* __restrict_
   }
   for (int s = s_own; s - lane < nsplit; s += kWaves * 64) {  // wave-uniform bound
     float2 st = st_own;
-    int4 t = top_own;
+    int2 t = top_own;
     if (s != s_own && s < nsplit) {  // splits past the first 64 kWaves (rare): read their records
       st = ml[(size_t)s * R];
       t = top[(size_t)s * R];
@@ -1075,8 +1073,8 @@ verify_combine_kernel(const float2* __restrict__ ws_ml, const float* __restrict_
       const int k = __ffsll((long long)pick) - 1;
       pick &= pick - 1;
       const float c = __shfl(coef, k, 64);
-      const uint64_t vrow = ((uint64_t)(uint32_t)__shfl(t.z, k, 64) << 32) | (uint32_t)__shfl(t.y, k, 64);
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint8_t*>(vrow) + lane * 16);
+      const int slot = min(max(__shfl(t.y, k, 64), 0), N - 1);  // clamped again: any workspace stays in the pool
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(kv_pool + (size_t)slot * kRowBytes + lane * 16);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         acc0[q] += c * (float)v[q];
@@ -1117,7 +1115,8 @@ constexpr int kQuarterWaves = 8;
 template <bool kBalanced>
 __global__ void __launch_bounds__(kQuarterWaves * 64)
 verify_combine_quarter_kernel(const float2* __restrict__ ws_ml, const float* __restrict__ ws_acc,
-                              const int4* __restrict__ ws_top, int B, int R, int nsplit_or_units,
+                              const int2* __restrict__ ws_top, const uint8_t* __restrict__ kv_pool, int N, int B,
+                              int R, int nsplit_or_units,
                               const int* __restrict__ split_start, __bf16* __restrict__ out,
                               float* __restrict__ lse) {
   __shared__ float red_m[kQuarterWaves];
@@ -1140,11 +1139,11 @@ verify_combine_quarter_kernel(const float2* __restrict__ ws_ml, const float* __r
     first = (size_t)b * nsplit;
   }
   const float2* ml = ws_ml + first * R + r;
-  const int4* top = ws_top + first * R + r;
+  const int2* top = ws_top + first * R + r;
   // 1. split w*64 + lane: (m, l) and top record in registers; the max over every split
   const int s_own = w * 64 + lane;
   const float2 st_own = s_own < nsplit ? ml[(size_t)s_own * R] : make_float2(-INFINITY, 0.0f);
-  const int4 top_own = s_own < nsplit ? top[(size_t)s_own * R] : make_int4(0, 0, 0, 0);
+  const int2 top_own = s_own < nsplit ? top[(size_t)s_own * R] : make_int2(0, 0);
   float M = st_own.x;
   for (int s = s_own + kQuarterWaves * 64; s < nsplit; s += kQuarterWaves * 64) M = fmaxf(M, ml[(size_t)s * R].x);
 #pragma unroll
@@ -1210,7 +1209,7 @@ verify_combine_quarter_kernel(const float2* __restrict__ ws_ml, const float* __r
   for (int k = 1; k < kQuarterWaves; ++k) den_row += red_den[k];
   for (int s = s_own; s - lane < nsplit; s += kQuarterWaves * 64) {  // wave-uniform bound
     float2 st = st_own;
-    int4 t = top_own;
+    int2 t = top_own;
     if (s != s_own && s < nsplit) {
       st = ml[(size_t)s * R];
       t = top[(size_t)s * R];
@@ -1225,8 +1224,8 @@ verify_combine_quarter_kernel(const float2* __restrict__ ws_ml, const float* __r
       const int k = __ffsll((long long)pick) - 1;
       pick &= pick - 1;
       const float c = __shfl(coef, k, 64);
-      const uint64_t vrow = ((uint64_t)(uint32_t)__shfl(t.z, k, 64) << 32) | (uint32_t)__shfl(t.y, k, 64);
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint8_t*>(vrow) + 2 * col0);
+      const int slot = min(max(__shfl(t.y, k, 64), 0), N - 1);
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(kv_pool + (size_t)slot * kRowBytes + 2 * col0);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         acc0[q] += c * (float)v[q];
@@ -1264,7 +1263,7 @@ constexpr long long kCombineFewRows = 512;
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Per partial row: (m, l), the 512 accumulators, and the top record {exact top probability (float
-// bits), value-row address low, high, 0}; each region 256-byte aligned.
+// bits), pool slot of its value row}; each region 256-byte aligned.
 struct WorkspaceLayout {
   size_t ml_bytes, acc_bytes, top_bytes;
 };
@@ -1273,7 +1272,7 @@ WorkspaceLayout workspace_layout(int B, int q_len, int H, int nsplit) {
   const size_t rows = (size_t)B * nsplit * q_len * H;
   return {align_up(rows * sizeof(float2), MLA_VERIFY_WORKSPACE_ALIGN),
           align_up(rows * kLatent * sizeof(float), MLA_VERIFY_WORKSPACE_ALIGN),
-          align_up(rows * sizeof(int4), MLA_VERIFY_WORKSPACE_ALIGN)};
+          align_up(rows * sizeof(int2), MLA_VERIFY_WORKSPACE_ALIGN)};
 }
 
 bool sizes_ok(int B, int q_len, int H) {
@@ -1293,7 +1292,7 @@ BalancedLayout balanced_layout(int B, int q_len, int H, int units) {
   return {align_up((size_t)units * sizeof(int4) + (size_t)(B + 1) * sizeof(int), MLA_VERIFY_WORKSPACE_ALIGN),
           align_up(rows * sizeof(float2), MLA_VERIFY_WORKSPACE_ALIGN),
           align_up(rows * kLatent * sizeof(float), MLA_VERIFY_WORKSPACE_ALIGN),
-          align_up(rows * sizeof(int4), MLA_VERIFY_WORKSPACE_ALIGN)};
+          align_up(rows * sizeof(int2), MLA_VERIFY_WORKSPACE_ALIGN)};
 }
 
 bool balanced_sizes_ok(int B, int q_len, int H, int units) {
@@ -1332,7 +1331,7 @@ namespace {
 struct Launch {
   float2* ws_ml;
   float* ws_acc;
-  int4* ws_top;
+  int2* ws_top;
   int R;
 };
 
@@ -1349,7 +1348,7 @@ Launch split_workspace(void* workspace, int B, int q_len, int H, int nsplit) {
   const WorkspaceLayout lay = workspace_layout(B, q_len, H, nsplit);
   uint8_t* w = static_cast<uint8_t*>(workspace);
   return {reinterpret_cast<float2*>(w), reinterpret_cast<float*>(w + lay.ml_bytes),
-          reinterpret_cast<int4*>(w + lay.ml_bytes + lay.acc_bytes), q_len * H};
+          reinterpret_cast<int2*>(w + lay.ml_bytes + lay.acc_bytes), q_len * H};
 }
 
 // The partial kernels gather rows with 32-bit byte offsets from the pool base when every offset they
@@ -1374,17 +1373,19 @@ int launch_partial(const void* q_nope, const void* q_rope, const void* kv_pool, 
   return hipGetLastError() == hipSuccess ? MLA_VERIFY_OK : MLA_VERIFY_ERR_LAUNCH;
 }
 
-int launch_combine(const Launch& ws, int B, int nsplit, void* out, float* lse, hipStream_t stream) {
+int launch_combine(const Launch& ws, const void* kv_pool, int64_t N, int B, int nsplit, void* out, float* lse,
+                   hipStream_t stream) {
+  const uint8_t* pool = static_cast<const uint8_t*>(kv_pool);
   const long long crows = (long long)B * ws.R;
   if (crows >= kCombineManyRows)
     hipLaunchKernelGGL((verify_combine_kernel<false, 1>), dim3((unsigned)((crows + 3) / 4)), dim3(256), 0, stream,
-                       ws.ws_ml, ws.ws_acc, ws.ws_top, B, ws.R, nsplit, nullptr, static_cast<__bf16*>(out), lse);
+                       ws.ws_ml, ws.ws_acc, ws.ws_top, pool, (int)N, B, ws.R, nsplit, nullptr, static_cast<__bf16*>(out), lse);
   else if (crows >= kCombineFewRows)
     hipLaunchKernelGGL((verify_combine_kernel<false, 4>), dim3((unsigned)crows), dim3(256), 0, stream, ws.ws_ml,
-                       ws.ws_acc, ws.ws_top, B, ws.R, nsplit, nullptr, static_cast<__bf16*>(out), lse);
+                       ws.ws_acc, ws.ws_top, pool, (int)N, B, ws.R, nsplit, nullptr, static_cast<__bf16*>(out), lse);
   else
     hipLaunchKernelGGL((verify_combine_quarter_kernel<false>), dim3((unsigned)(4 * crows)), dim3(kQuarterWaves * 64), 0,
-                       stream, ws.ws_ml, ws.ws_acc, ws.ws_top, B, ws.R, nsplit, nullptr, static_cast<__bf16*>(out),
+                       stream, ws.ws_ml, ws.ws_acc, ws.ws_top, pool, (int)N, B, ws.R, nsplit, nullptr, static_cast<__bf16*>(out),
                        lse);
   return hipGetLastError() == hipSuccess ? MLA_VERIFY_OK : MLA_VERIFY_ERR_LAUNCH;
 }
@@ -1394,7 +1395,7 @@ struct BalancedLaunch {
   int4* split_info;
   float2* ws_ml;
   float* ws_acc;
-  int4* ws_top;
+  int2* ws_top;
   int R;
 };
 
@@ -1413,7 +1414,7 @@ BalancedLaunch balanced_workspace(void* workspace, int B, int q_len, int H, int 
   uint8_t* w = static_cast<uint8_t*>(workspace);
   return {reinterpret_cast<int*>(w + (size_t)units * sizeof(int4)), reinterpret_cast<int4*>(w),
           reinterpret_cast<float2*>(w + lay.plan_bytes), reinterpret_cast<float*>(w + lay.plan_bytes + lay.ml_bytes),
-          reinterpret_cast<int4*>(w + lay.plan_bytes + lay.ml_bytes + lay.acc_bytes), q_len * H};
+          reinterpret_cast<int2*>(w + lay.plan_bytes + lay.ml_bytes + lay.acc_bytes), q_len * H};
 }
 
 int launch_balanced_partial(const void* q_nope, const void* q_rope, const void* kv_pool, int64_t N,
@@ -1438,17 +1439,19 @@ int launch_balanced_partial(const void* q_nope, const void* q_rope, const void* 
   return hipGetLastError() == hipSuccess ? MLA_VERIFY_OK : MLA_VERIFY_ERR_LAUNCH;
 }
 
-int launch_balanced_combine(const BalancedLaunch& ws, int B, int units, void* out, float* lse, hipStream_t stream) {
+int launch_balanced_combine(const BalancedLaunch& ws, const void* kv_pool, int64_t N, int B, int units, void* out,
+                            float* lse, hipStream_t stream) {
+  const uint8_t* pool = static_cast<const uint8_t*>(kv_pool);
   const long long crows = (long long)B * ws.R;
   if (crows >= kCombineManyRows)
     hipLaunchKernelGGL((verify_combine_kernel<true, 1>), dim3((unsigned)((crows + 3) / 4)), dim3(256), 0, stream,
-                       ws.ws_ml, ws.ws_acc, ws.ws_top, B, ws.R, units, (const int*)ws.split_start, static_cast<__bf16*>(out), lse);
+                       ws.ws_ml, ws.ws_acc, ws.ws_top, pool, (int)N, B, ws.R, units, (const int*)ws.split_start, static_cast<__bf16*>(out), lse);
   else if (crows >= kCombineFewRows)
     hipLaunchKernelGGL((verify_combine_kernel<true, 4>), dim3((unsigned)crows), dim3(256), 0, stream, ws.ws_ml,
-                       ws.ws_acc, ws.ws_top, B, ws.R, units, (const int*)ws.split_start, static_cast<__bf16*>(out), lse);
+                       ws.ws_acc, ws.ws_top, pool, (int)N, B, ws.R, units, (const int*)ws.split_start, static_cast<__bf16*>(out), lse);
   else
     hipLaunchKernelGGL((verify_combine_quarter_kernel<true>), dim3((unsigned)(4 * crows)), dim3(kQuarterWaves * 64), 0,
-                       stream, ws.ws_ml, ws.ws_acc, ws.ws_top, B, ws.R, units, (const int*)ws.split_start,
+                       stream, ws.ws_ml, ws.ws_acc, ws.ws_top, pool, (int)N, B, ws.R, units, (const int*)ws.split_start,
                        static_cast<__bf16*>(out), lse);
   return hipGetLastError() == hipSuccess ? MLA_VERIFY_OK : MLA_VERIFY_ERR_LAUNCH;
 }
@@ -1475,13 +1478,15 @@ extern "C" int mla_verify_attn_partial(const void* q_nope, const void* q_rope, c
                         B, q_len, H, scale, nsplit, split_workspace(workspace, B, q_len, H, nsplit), stream);
 }
 
-extern "C" int mla_verify_attn_combine(const void* workspace, size_t workspace_bytes, int B, int q_len, int H,
-                                       int nsplit, void* out, float* lse, hipStream_t stream) {
-  if (!out || !lse) return MLA_VERIFY_ERR_NULL;
+extern "C" int mla_verify_attn_combine(const void* workspace, size_t workspace_bytes, const void* kv_pool, int64_t N,
+                                       int B, int q_len, int H, int nsplit, void* out, float* lse,
+                                       hipStream_t stream) {
+  if (!out || !lse || !kv_pool) return MLA_VERIFY_ERR_NULL;
+  if (N < 1 || N > INT32_MAX) return MLA_VERIFY_ERR_SHAPE;
   const int rc = check_common(B, q_len, H, nsplit, workspace, workspace_bytes);
   if (rc != MLA_VERIFY_OK) return rc;
-  return launch_combine(split_workspace(const_cast<void*>(workspace), B, q_len, H, nsplit), B, nsplit, out, lse,
-                        stream);
+  return launch_combine(split_workspace(const_cast<void*>(workspace), B, q_len, H, nsplit), kv_pool, N, B, nsplit,
+                        out, lse, stream);
 }
 
 extern "C" int mla_verify_attn(const void* q_nope, const void* q_rope, const void* kv_pool, int64_t N,
@@ -1500,7 +1505,7 @@ extern "C" int mla_verify_attn(const void* q_nope, const void* q_rope, const voi
   rc = launch_partial(q_nope, q_rope, kv_pool, N, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr, B,
                       q_len, H, scale, nsplit, ws, stream);
   if (rc != MLA_VERIFY_OK) return rc;
-  return launch_combine(ws, B, nsplit, out, lse, stream);
+  return launch_combine(ws, kv_pool, N, B, nsplit, out, lse, stream);
 }
 
 extern "C" int mla_verify_attn_balanced_partial(const void* q_nope, const void* q_rope, const void* kv_pool,
@@ -1520,13 +1525,15 @@ extern "C" int mla_verify_attn_balanced_partial(const void* q_nope, const void* 
                                  balanced_workspace(workspace, B, q_len, H, units), stream);
 }
 
-extern "C" int mla_verify_attn_balanced_combine(const void* workspace, size_t workspace_bytes, int B, int q_len,
-                                                int H, int units, void* out, float* lse, hipStream_t stream) {
-  if (!out || !lse) return MLA_VERIFY_ERR_NULL;
+extern "C" int mla_verify_attn_balanced_combine(const void* workspace, size_t workspace_bytes, const void* kv_pool,
+                                                int64_t N, int B, int q_len, int H, int units, void* out, float* lse,
+                                                hipStream_t stream) {
+  if (!out || !lse || !kv_pool) return MLA_VERIFY_ERR_NULL;
+  if (N < 1 || N > INT32_MAX) return MLA_VERIFY_ERR_SHAPE;
   const int rc = check_balanced(B, q_len, H, units, workspace, workspace_bytes);
   if (rc != MLA_VERIFY_OK) return rc;
-  return launch_balanced_combine(balanced_workspace(const_cast<void*>(workspace), B, q_len, H, units), B, units, out,
-                                 lse, stream);
+  return launch_balanced_combine(balanced_workspace(const_cast<void*>(workspace), B, q_len, H, units), kv_pool, N, B,
+                                 units, out, lse, stream);
 }
 
 extern "C" int mla_verify_attn_balanced(const void* q_nope, const void* q_rope, const void* kv_pool, int64_t N,
@@ -1545,5 +1552,5 @@ extern "C" int mla_verify_attn_balanced(const void* q_nope, const void* q_rope, 
   rc = launch_balanced_partial(q_nope, q_rope, kv_pool, N, kv_indptr, kv_indices, out_cache_loc, custom_mask,
                                mask_indptr, B, q_len, H, scale, units, ws, stream);
   if (rc != MLA_VERIFY_OK) return rc;
-  return launch_balanced_combine(ws, B, units, out, lse, stream);
+  return launch_balanced_combine(ws, kv_pool, N, B, units, out, lse, stream);
 }

@@ -42,3 +42,26 @@ def brute_force(q_nope, q_rope, pool, kv_indptr, kv_indices, out_cache_loc, cust
                                 for e in range(512)]
                 lse[b][i][h] = l
     return out, lse
+
+
+def brute_force_weights(q_nope, q_rope, pool, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr, scale,
+                        b, i, h):
+    """Softmax weights of row (b, i, h) over its columns: exp(s_c - lse) where visible, 0 where masked."""
+    q_len = q_nope.shape[1]
+    start, end = int(kv_indptr[b]), int(kv_indptr[b + 1])
+    prefix = end - start
+    length = prefix + q_len
+    slots = [int(kv_indices[start + c]) for c in range(prefix)]
+    slots += [int(out_cache_loc[b * q_len + t]) for t in range(q_len)]
+    q = [_bf16(x) for x in q_nope[b, i, h]] + [_bf16(x) for x in q_rope[b, i, h]]
+    row0 = int(mask_indptr[b]) + i * length
+    scores = {}
+    for c in range(length):
+        if int(custom_mask[row0 + c]) != 0:
+            key = [_bf16(x) for x in pool[slots[c]]]
+            scores[c] = scale * math.fsum(q[d] * key[d] for d in range(576))
+    if not scores:
+        return [0.0] * length
+    m = max(scores.values())
+    lse = m + math.log(math.fsum(math.exp(s - m) for s in scores.values()))
+    return [math.exp(scores[c] - lse) if c in scores else 0.0 for c in range(length)]

@@ -34,9 +34,9 @@ def test_library_exports_every_declared_function():
 
 
 def test_workspace_size():
-    # (m, l) float2 + 512 fp32 per (b, split, token, head), each region padded to 256 bytes
+    # (m, l) float2 + 512 fp32 + an 8-byte top record per (b, split, token, head), each region padded to 256 bytes
     rows = 2 * 16 * 9 * 8
-    expect = -(-rows * 8 // 256) * 256 + -(-rows * 2048 // 256) * 256 + -(-rows * 16 // 256) * 256
+    expect = -(-rows * 8 // 256) * 256 + -(-rows * 2048 // 256) * 256 + -(-rows * 8 // 256) * 256
     assert pkg.workspace_size(2, 9, 8, 16) == expect
     assert pkg.workspace_size(0, 9, 8, 16) == 0
     assert pkg.workspace_size(1, 0, 8, 16) == 0
@@ -94,9 +94,11 @@ def test_phase_entry_points_validate():
     assert pkg.partial_raw(*base[:2], None, *base[3:]) == -1
     assert pkg.partial_raw(*base[:13], 0, *base[14:]) == -3
     assert pkg.partial_raw(*base[:15], ws_bytes - 1, None) == -4
-    assert pkg.combine_raw(0x100000, ws_bytes, 1, 9, 8, 4, None, FAKE, None) == -1
-    assert pkg.combine_raw(0x100000, ws_bytes, 1, 9, 8, 5, FAKE, FAKE, None) == -4
-    assert pkg.combine_raw(0x100000, ws_bytes, 0, 9, 8, 4, FAKE, FAKE, None) == -2
+    assert pkg.combine_raw(0x100000, ws_bytes, FAKE, 100, 1, 9, 8, 4, None, FAKE, None) == -1
+    assert pkg.combine_raw(0x100000, ws_bytes, None, 100, 1, 9, 8, 4, FAKE, FAKE, None) == -1  # pool needed
+    assert pkg.combine_raw(0x100000, ws_bytes, FAKE, 0, 1, 9, 8, 4, FAKE, FAKE, None) == -2
+    assert pkg.combine_raw(0x100000, ws_bytes, FAKE, 100, 1, 9, 8, 5, FAKE, FAKE, None) == -4
+    assert pkg.combine_raw(0x100000, ws_bytes, FAKE, 100, 0, 9, 8, 4, FAKE, FAKE, None) == -2
 
 
 def test_tree_mask_validates_before_any_hip_call():
@@ -120,7 +122,7 @@ def test_kv_compact_validates_before_any_hip_call():
 def test_balanced_workspace_size_and_validation():
     rows = 40 * 16 * 64
     plan = -(-(40 * 16 + 5 * 4) // 256) * 256
-    expect = plan + -(-rows * 8 // 256) * 256 + -(-rows * 2048 // 256) * 256 + -(-rows * 16 // 256) * 256
+    expect = plan + -(-rows * 8 // 256) * 256 + -(-rows * 2048 // 256) * 256 + -(-rows * 8 // 256) * 256
     assert pkg.balanced_workspace_size(4, 16, 64, 40) == expect
     assert pkg.balanced_workspace_size(4, 16, 64, 3) == 0          # fewer units than requests
     assert pkg.balanced_workspace_size(4, 16, 64, 4097) == 0
@@ -135,8 +137,10 @@ def test_balanced_workspace_size_and_validation():
     assert pkg.balanced_raw(**{**base, "B": 4097}) == -2
     assert pkg.balanced_raw(**{**base, "workspace_bytes": ws - 1}) == -4
     assert pkg.balanced_raw(**{**base, "workspace": 0x100010}) == -4
-    assert pkg.balanced_combine_raw(0x100000, ws, 2, 9, 8, 8, None, FAKE, None) == -1
-    assert pkg.balanced_combine_raw(0x100000, ws - 1, 2, 9, 8, 8, FAKE, FAKE, None) == -4
+    assert pkg.balanced_combine_raw(0x100000, ws, FAKE, 100, 2, 9, 8, 8, None, FAKE, None) == -1
+    assert pkg.balanced_combine_raw(0x100000, ws, None, 100, 2, 9, 8, 8, FAKE, FAKE, None) == -1
+    assert pkg.balanced_combine_raw(0x100000, ws, FAKE, 2**31, 2, 9, 8, 8, FAKE, FAKE, None) == -2
+    assert pkg.balanced_combine_raw(0x100000, ws - 1, FAKE, 100, 2, 9, 8, 8, FAKE, FAKE, None) == -4
 
 
 def test_check_workspace_sizes():

@@ -163,14 +163,33 @@ def test_balanced_graph_replays_match_eager():
         pkg.verify_attn(call.q_nope, call.q_rope, call.pool, call.kv_indptr, call.kv_indices, call.out_cache_loc,
                         call.custom_mask, call.mask_indptr, inp.scale, units, ws, call.out, call.lse, stream=stream,
                         balanced=True)
+    o_ref, l_ref = _oracle_full(inp)
     for k in range(4):
         call.out.fill_(float("nan"))
         ws.fill_(0xFF)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
+        o, l = call.host()
+        compare(o, l, o_ref, l_ref, f"replay {k}")
         assert torch.equal(call.out.view(torch.int16), ref_out.view(torch.int16)), f"replay {k}"
         assert torch.equal(call.lse, ref_lse)
+
+
+def test_ragged_185k_every_row():
+    """Every one of the 4096 output rows of the ragged batch (prefixes 4096/32768/120000/185000,
+    q_len 16, H 64) against the oracle, under the benchmark's schedule (balanced, 32 units) and the
+    per-request schedule with nsplit 64."""
+    wl = W.CONFIGS["ragged4_185k_h64"]
+    inp = W.make_inputs(wl)
+    _say(f"[balanced] {wl.name}: full oracle (every row)")
+    ref_out, ref_lse = _oracle_full(inp)
+    call = DeviceCall(inp)
+    for balanced, ns in ((True, 32), (False, 64)):
+        _say(f"[balanced] {wl.name} every row, balanced={balanced} {ns}")
+        call.run(ns, balanced=balanced)
+        got_out, got_lse = call.host()
+        compare(got_out, got_lse, ref_out, ref_lse, f"{wl.name} balanced={balanced} {ns}")
 
 
 @pytest.mark.parametrize("name,layout,units", [("4k_h64", None, 51), ("16k_h64", "contiguous", 51),

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import workloads as W
-from bruteforce import brute_force
+from bruteforce import brute_force, brute_force_weights
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -220,6 +220,56 @@ def test_weights_sum_to_one():
         mask = _mask(inp, b)[i]
         assert abs(math.fsum(w) - 1.0) <= 1e-12
         assert np.all(w[mask == 0] == 0) and np.all(w[mask != 0] > 0)
+
+
+@pytest.mark.parametrize("seed,prefixes,q_len,H,rows", [
+    (26, (37,), 5, 2, [(0, 0, 0), (0, 4, 1), (0, 2, 1)]),
+    (27, (9, 0, 21), 4, 3, [(0, 3, 2), (1, 1, 0), (2, 0, 1)]),
+])
+def test_row_weights_match_brute_force(seed, prefixes, q_len, H, rows):
+    """Each weight, not just their sum and support, against the independent brute force's exp(s - lse);
+    half of every row's columns are hidden by a random mask so the zero pattern is checked too."""
+    inp = _mk(seed, prefixes, q_len, H)
+    rng = np.random.default_rng(seed)
+    inp.custom_mask = (rng.random(inp.custom_mask.shape) < 0.5).astype(np.uint8)
+    pool = W.full_pool(inp)
+    args = oracle.inputs_args(inp, pool)
+    for b, i, h in rows:
+        w = oracle.row_weights(*args, b=b, i=i, h=h)
+        ref = np.array(brute_force_weights(*args, b, i, h))
+        assert np.array_equal(w == 0, ref == 0), (b, i, h)
+        assert np.abs(w - ref).max() <= 1e-12 * max(ref.max(), 1e-300), (b, i, h)
+
+
+def test_row_weights_planted_mistake_is_caught(tmp_path):
+    """exp(m - s) normalised by its own sum keeps the sum (1) and the support of the true weights: the
+    old sum/support pin cannot tell, the element-wise pin above must."""
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "mla_verify_oracle.c")).read()
+    old = "weights[c] == -INFINITY ? 0.0 : exp(weights[c] - m) / z"
+    assert src.count(old) == 1
+    mutated = src.replace(old, "weights[c] == -INFINITY ? 0.0 : exp(m - weights[c]) / z2")
+    mutated = mutated.replace("for (int c = 0; c < L; ++c) weights[c] = weights[c] == -INFINITY",
+                              "double z2 = 0.0;\n    for (int c = 0; c < L; ++c) if (weights[c] != -INFINITY) "
+                              "z2 += exp(m - weights[c]);\n    for (int c = 0; c < L; ++c) weights[c] = "
+                              "weights[c] == -INFINITY")
+    (tmp_path / "m.c").write_text(mutated)
+    so = tmp_path / "m.so"
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-shared", "-fPIC", "-o", str(so), str(tmp_path / "m.c"), "-lm"],
+                   check=True)
+    lib = ctypes.CDLL(str(so))
+    vp, i64, i32, dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
+    lib.mla_oracle_row_weights.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, vp, i32, i32, i32, dbl, i32, i32, i32, vp]
+    inp = _mk(26, (37,), 5, 2)
+    pool = W.full_pool(inp)
+    args = oracle.inputs_args(inp, pool)
+    a = oracle._Args(*args)
+    L = inp.prefixes[0] + inp.q_len
+    w = np.empty(L)
+    assert lib.mla_oracle_row_weights(*a.head(), 0, 2, 1, oracle._ptr(w)) == 0
+    mask = _mask(inp, 0)[2]
+    assert abs(math.fsum(w) - 1.0) <= 1e-12 and np.all((w > 0) == (mask != 0))   # the old pin passes
+    ref = np.array(brute_force_weights(*args, 0, 2, 1))
+    assert np.abs(w - ref).max() > 1e-6                                         # the new one does not
 
 
 def test_duplicate_slots_count_twice():

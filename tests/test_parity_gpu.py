@@ -344,6 +344,8 @@ def test_graph_capture_replay_matches_eager():
             pkg.verify_attn(call.q_nope, call.q_rope, call.pool, call.kv_indptr, call.kv_indices,
                             call.out_cache_loc, call.custom_mask, call.mask_indptr, inp.scale, 16, ws, call.out,
                             call.lse)
+    ref_out, ref_lse = _oracle_full(inp)
+    compare(eager_out, eager_lse, ref_out, ref_lse, "eager")
     for rep in range(5):
         call.out.fill_(float("nan"))
         ws.fill_(0xFF)
@@ -351,6 +353,7 @@ def test_graph_capture_replay_matches_eager():
         g.replay()
         torch.cuda.synchronize()
         o, l = call.host()
+        compare(o, l, ref_out, ref_lse, f"replay {rep}")
         assert np.array_equal(o, eager_out) and np.array_equal(l, eager_lse), f"replay {rep}"
 
 

@@ -15,7 +15,8 @@ if not torch.cuda.is_available():
 
 import speculative_decoding_mla_split_amd as pkg  # noqa: E402
 
-from gpu_harness import DeviceCall  # noqa: E402
+from gpu_harness import DeviceCall, compare  # noqa: E402
+import oracle  # noqa: E402
 
 DEV = torch.device("cuda:0")
 FILL = 0xAB  # bytes the builder must not touch keep this value
@@ -175,6 +176,13 @@ def test_device_mask_drives_attention_and_graph_replays():
         torch.cuda.synchronize()
         assert torch.equal(got_out.view(torch.int16), dc.out.view(torch.int16)), f"replay {k}: out"
         assert torch.equal(got_lse, dc.lse), f"replay {k}: lse"
+        # and the replay's output against the oracle on the same trees' mask
+        pool, ki, oc = W.compact_inputs(inp)
+        args = list(oracle.inputs_args(inp, pool, ki, oc))
+        args[6] = ref_masks[k % 3]
+        ref_out, ref_lse = oracle.attn(*args)
+        compare(got_out.float().cpu().numpy(), got_lse.cpu().numpy().astype(np.float64), ref_out, ref_lse,
+                f"replay {k} vs oracle")
 
 
 def _bf16_pool(arr):

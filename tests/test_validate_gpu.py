@@ -10,7 +10,7 @@ import torch
 import oracle
 import speculative_decoding_mla_split_amd as pkg
 import workloads as W
-from gpu_harness import DeviceCall
+from gpu_harness import DeviceCall, compare
 
 pytestmark = pytest.mark.gpu
 
@@ -119,6 +119,8 @@ def test_validate_entry_point_and_graph_replays():
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         go()
+    pool, ki, oc = W.compact_inputs(inp)
+    ref_out, ref_lse = oracle.attn(*oracle.inputs_args(inp, pool, ki, oc))
     for k in range(4):
         rep.fill_(-1.0)
         call.out.fill_(0.0)
@@ -127,6 +129,8 @@ def test_validate_entry_point_and_graph_replays():
         torch.cuda.synchronize()
         assert torch.equal(rep, eager), f"replay {k}: {rep.tolist()} vs {eager.tolist()}"
         assert torch.equal(call.out.view(torch.int16), out_eager.view(torch.int16))
+        o, l = call.host()
+        compare(o, l, ref_out, ref_lse, f"validate replay {k} vs oracle")
 
 
 def test_check_of_balanced_schedule_on_ragged_185k():
