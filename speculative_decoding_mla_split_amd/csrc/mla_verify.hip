@@ -7,9 +7,10 @@
 //   verify_partial_kernel  one workgroup per (request, split, 128-row tile). The 576-wide bf16 KV
 //                          rows of the split are gathered through the two index arrays straight
 //                          into LDS with 16-byte direct-to-LDS loads (three-deep ring of 32-row
-//                          tiles), shared by all 128 query rows (2 wave pairs x 64 rows). QK^T and
+//                          tiles), shared by all 128 query rows (4 waves x 32 rows). QK^T and
 //                          PV run on 32x32x16 bf16 MFMA with fp32 accumulation; the mask lookup
-//                          and online softmax happen in registers between the two.
+//                          and the softmax of one tile run in registers between the score
+//                          products of the next.
 //   verify_combine_kernel  log-sum-exp combine of each query row's partials into the bf16 output
 //                          and the fp32 natural-log LSE (one, four or, below 512 rows, a quarter
 //                          row per workgroup).
@@ -19,13 +20,15 @@
 //   S^T[c][r] = K[c][:] . Q[r][:]  (A = K from LDS, B = Q resident in VGPRs)
 //   O^T[e][r] += V^T[e][c] . P^T[c][r]  (A = V^T via ds_read_b64_tr_b16, B = P^T from registers)
 // so each lane holds one query row (lane % 32) for both S^T and O^T, and the softmax statistics
-// never leave the lane (only the lane pair l, l^32 shares a row). A wave scores one such block
-// over the whole row and accumulates the output of two (its own and its partner's) over half the
-// output columns, so every V fragment it reads from LDS feeds two MFMAs.
+// never leave the lane (only the lane pair l, l^32 shares a row). A wave scores its block over the
+// whole row and accumulates the block's whole 512-wide output, so the four waves exchange nothing
+// but the KV tiles they load together.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "mla_verify.h"
 
@@ -36,11 +39,9 @@ constexpr int kRope = MLA_VERIFY_ROPE;
 constexpr int kRowBytes = MLA_VERIFY_ROW * 2;  // 1152
 constexpr int kChunks = kRowBytes / 16;        // 72 sixteen-byte chunks per KV row
 constexpr int kTile = 32;                      // KV columns per LDS tile
-constexpr int kPairs = 2;                      // wave pairs per workgroup
-constexpr int kWaves = 2 * kPairs;
+constexpr int kWaves = 4;                      // waves per workgroup, one 32-row block each
 constexpr int kBlockRows = 32;                 // query rows per MFMA block (one lane per row)
-constexpr int kRowsPerPair = 2 * kBlockRows;   // 64: a pair holds two row blocks
-constexpr int kRowsPerWG = kPairs * kRowsPerPair;        // 128
+constexpr int kRowsPerWG = kWaves * kBlockRows;          // 128
 constexpr int kBufs = 3;                                 // LDS ring depth
 // LDS tile layout. Loader wave w owns tile rows [8w, 8w+8) in region w; a region holds 9 groups
 // (16-byte chunks 8j .. 8j+7 of all its 8 rows, 128 bytes per row), so one direct-to-LDS
@@ -52,9 +53,10 @@ constexpr int kTileBytes = 4 * kRegionBytes;             // 37376
 constexpr int kLoaders = 4;                              // waves that gather KV rows
 constexpr int kRowsPerLoader = kTile / kLoaders;         // 8
 constexpr int kLoadsPerWave = kRowsPerLoader * kChunks / 64;  // 9 direct-to-LDS loads
-constexpr int kHalfSteps = (kLatent + kRope) / 32;       // 18 k-steps of 16 per half of the row
-constexpr int kHalfEBlocks = kLatent / 64;               // 8 blocks of 32 output columns per half
-constexpr int kPXchgBytes = 64 * 16 * 2;                 // one 32x32 block of bf16 probabilities
+constexpr int kSteps = (kLatent + kRope) / 16;           // 36 k-steps of 16 over the 576-wide row
+constexpr int kRegSteps = kLatent / 16;                  // 32 of them (the latent part) keep Q in VGPRs
+constexpr int kQRopeBytes = (kSteps - kRegSteps) * 64 * 16;  // a wave's rope Q operands in LDS (4 KB)
+constexpr int kEBlocks = kLatent / 32;                   // 16 blocks of 32 output columns
 constexpr float kHeadroom = 64.0f;  // scores may exceed a row's reference max by this (log2 units)
 // Per-tile metadata of one wave, all through byte-granular direct-to-LDS loads (each byte lands
 // zero-extended in its own dword): load 0 carries the 4 bytes of each of the 8 slot indices of the
@@ -65,7 +67,7 @@ constexpr int kMetaExtra = 2;                    // extra mask loads at most (bl
 constexpr int kMetaTokens = 1 + 2 * kMetaExtra;  // block tokens whose mask bytes ride in LDS
 constexpr int kMetaBytes = 256 * (1 + kMetaExtra);
 constexpr int kMetaStages = 8;                   // per-wave ring of per-tile metadata
-constexpr int kLdsBytes = kBufs * kTileBytes + kWaves * (2 * kPXchgBytes + kMetaStages * kMetaBytes);
+constexpr int kLdsBytes = kBufs * kTileBytes + kWaves * (kMetaStages * kMetaBytes + kQRopeBytes);
 
 static_assert(kRowsPerLoader * kChunks % 64 == 0, "loader must tile whole wave instructions");
 static_assert(kWaves == kLoaders, "every wave gathers a share of each tile");
@@ -81,6 +83,17 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Compile-time loop: f(std::integral_constant<int, I>{}) for I = B .. E-1, so code that branches on
+// the index (which softmax piece or load goes between which matrix products) is resolved while
+// compiling rather than left to the optimiser after unrolling.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // XOR swizzle inside a group: logical chunk k of tile row c sits in slot (k % 8) ^ swz(c) of group
 // k / 8. With all three row bits in the XOR, the eight rows of a region put any one logical chunk in
@@ -169,9 +182,10 @@ __device__ __forceinline__ Split decode_unit(int B, int nsplit, int n_rt) {
 struct Ctx {
   size_t mask_base;
   int N, b, q_len, kv_start, P, L, c_end;
-  int lane, g, hf;
+  int lane, g;
   int loader_row0;
   int tok_first, tok_last, my_pair, my_half, n_tok_pairs;
+  bool uniform_token;  // the wave's 32 rows all belong to one draft token (wave-uniform)
   int n_meta;  // metadata loads per tile of this wave: 1 + extra mask loads (wave-uniform)
   float scale_log2;
 };
@@ -225,10 +239,12 @@ __device__ __forceinline__ void kv_gather_group(const KvGather& k) {
   else
     dma_group<J>(k.base, k.voff, k.m0);
 }
-__device__ __forceinline__ KvGather kv_gather_setup(const Ctx& x, const uint8_t* kv_pool, const uint8_t* slots,
-                                                    uint8_t* dst) {
+// The four slot bytes of the gather row this lane serves (one per dword in the metadata ring).
+__device__ __forceinline__ u32x4 kv_slot_bytes(const Ctx& x, const uint8_t* slots) {
+  return *reinterpret_cast<const u32x4*>(slots + 16 * (x.lane >> 3));
+}
+__device__ __forceinline__ KvGather kv_gather_build(const Ctx& x, const uint8_t* kv_pool, u32x4 sb, uint8_t* dst) {
   const int rho = x.lane >> 3, p = x.lane & 7;
-  const uint32_t* sb = reinterpret_cast<const uint32_t*>(slots + 16 * rho);  // 4 bytes, one per dword
   const int raw_slot = (int)(sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24));
   const int slot = min(max(raw_slot, 0), x.N - 1);
   KvGather k;
@@ -237,6 +253,10 @@ __device__ __forceinline__ KvGather kv_gather_setup(const Ctx& x, const uint8_t*
   k.base = kv_pool;
   k.m0 = lds_addr(dst + (x.loader_row0 / 8) * kRegionBytes);
   return k;
+}
+__device__ __forceinline__ KvGather kv_gather_setup(const Ctx& x, const uint8_t* kv_pool, const uint8_t* slots,
+                                                    uint8_t* dst) {
+  return kv_gather_build(x, kv_pool, kv_slot_bytes(x, slots), dst);
 }
 template <bool kWide, int J0, int J1>
 __device__ __forceinline__ void kv_gather_groups(const KvGather& k) {
@@ -287,213 +307,261 @@ struct Glob {
   const uint8_t* custom_mask;
 };
 
-// LDS areas of one wave: the shared tile ring, its private metadata ring, and its lane's entries in
-// the two probability exchange slots (step parity) of its own and its partner's.
+// LDS areas of one wave: the shared tile ring, its private metadata ring and its rope query operands
+// (k-step 32 + j of lane l at q_rope + 1024 j + 16 l).
 struct Bufs {
   uint8_t* kv;
   uint8_t* meta;
-  uint8_t* p_mine;
-  const uint8_t* p_other;
+  const uint8_t* q_rope;
 };
 
-// One 32-column tile for one wave. The wave holds the whole 576-wide query row of its own block
-// (rows 32hf .. 32hf+31 of the pair; q) and its half hf of the 512-wide output row of both blocks
-// of the pair (oacc[0] own, oacc[1] the partner's).
-//   1. scores of the own block over the whole row: 36 MFMAs, one per K fragment
-//   2. mask + softmax numerators of the own block against its fixed reference max
-//   3. the bf16 probabilities go to LDS (slot t % 2); after the barrier the partner's are read
-//   4. O^T of both blocks over the output half: each V fragment is read once and feeds two MFMAs
-// One barrier per step, and it also orders the tile ring:
-//  - it comes after every wave's PV of step t-1, so ring buffer (t+2) % 3, which held tile t-1, is
-//    free once it has passed;
-//  - before it each wave waits for all its loads (vmcnt(0)): the row loads of tile t+1 it issued in
-//    step t-1; after it tile t+1 is whole in LDS for every wave, ready for step t+1;
-//  - the probability slots alternate with the step, so a wave writing step t+1's probabilities
-//    cannot overwrite step t's before its partner has read them (it read them before arriving at
-//    the barrier of step t+1).
-// Hence the step issues the 9 row loads of tile t+2 and the metadata loads of tile t+4 in the PV
-// phase, between the MFMAs, after the barrier; a load has about one step to land. Scoring the own
-// block over the whole row makes every K fragment feed one MFMA (36.8 KB of K reads per wave and
-// tile), but needs no exchange of partial scores and so no second barrier, which costs more.
-// The LDS pointers are restrict-qualified: the buffers written by direct-to-LDS loads here are
-// never the ones read here, which lets the compiler drop its own blanket wait on those loads.
+// Running softmax state of the lane's query row over one split (see tile_iter).
+struct RowStats {
+  float m_ref;     // reference max (base-2 units of the scaled score), fixed once set
+  float l_lane;    // the lane's share of the row sum of 2^(score - m_ref)
+  float best_raw;  // the lane's largest visible raw score (element index in its low bits)
+  int best_col;    // and its column
+  bool over;       // a score exceeded m_ref + kHeadroom
+};
+
+// The score product S^T = K . Q^T of a tile accumulates in VGPRs through inline assembly. With the
+// 256 output accumulators in AGPRs, the compiler's own form of this product takes its accumulator in
+// AGPRs as well and so moves an output block out to VGPRs and back around every tile (48 register
+// moves per tile); this hipcc crashes on its option that selects the VGPR form. What the compiler
+// does not see through the asm: (1) a product that adds onto the previous product's result (the
+// same registers, the same instruction) needs no wait states, the matrix core forwards it; (2) a
+// vector instruction may read the accumulator only some 20 wait states after the last product,
+// which the loop guarantees by reading a score block one PV phase (32 products) after it was
+// finished, and qk_settle() provides where a read follows at once. The K operand registers are
+// written by LDS reads, whose completion the compiler tracks through the asm operands as for any
+// other instruction.
+__device__ __forceinline__ void qk_first(f32x16& s, const bf16x8& k, const bf16x8& q) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(k), "v"(q));
+}
+__device__ __forceinline__ void qk_next(f32x16& s, const bf16x8& k, const bf16x8& q) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(k), "v"(q));
+}
+__device__ __forceinline__ void qk_settle(f32x16& s) { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s)); }
+
+// Query (B) operand of k-step ks: the latent k-steps live in VGPRs, the four rope k-steps in LDS
+// (freeing 16 VGPRs the pipelined loop needs).
+template <int KS>
+__device__ __forceinline__ bf16x8 q_operand(const bf16x8 (&q)[kRegSteps], const Bufs& bf, int lane) {
+  if constexpr (KS < kRegSteps)
+    return q[KS];
+  else
+    return *reinterpret_cast<const bf16x8*>(bf.q_rope + 1024 * (KS - kRegSteps) + 16 * lane);
+}
+
+// K operand of k-step ks (logical chunk 2ks + g of tile row lane & 31) at kb + k_off[ks % 4] +
+// 1024 (ks / 4); the four per-lane offsets do not change from tile to tile.
+__device__ __forceinline__ bf16x8 load_k(const uint8_t* kb, const int (&k_off)[4], int ks) {
+  return *reinterpret_cast<const bf16x8*>(kb + k_off[ks % 4] + kGroupBytes * (ks / 4));
+}
+
+// V^T operand of output block eb (latent columns [32 eb, 32 eb + 32)) and k-step kk (tile columns
+// [16 kk, 16 kk + 16), permuted as the probabilities are): two transposed 8-byte reads, rows
+// 16 kk + 8m + v_row of latent chunk 4 eb + v_chunk (see run_split for v_off).
+__device__ __forceinline__ bf16x8 load_v(const uint8_t* kb, const int (&v_off)[2], int kk, int eb) {
+  const uint8_t* p0 = kb + v_off[eb & 1] + 2 * kk * kRegionBytes + kGroupBytes * (eb >> 1);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + kRegionBytes));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Visibility word of the lane's row for columns tile_c0 .. tile_c0 + 31 when all 32 rows of the
+// block belong to one draft token (H a multiple of 32): every lane reads the mask byte of column
+// lane % 32 from the metadata ring and one compare gives the whole word.
+__device__ __forceinline__ int mask_byte_uniform(const Ctx& x, const uint8_t* m) {
+  return *reinterpret_cast<const int*>(m + 128 + 4 * (x.lane & 31));
+}
+__device__ __forceinline__ uint32_t mask_word_uniform(const Ctx& x, int byte_val, int tile_c0) {
+  const bool col_ok = tile_c0 + (x.lane & 31) < x.c_end;
+  return (uint32_t)__ballot(col_ok && byte_val != 0);
+}
+
+// One pipelined tile step of one wave (the wave owns query rows 32w .. 32w+31 of the row tile: the
+// whole 576-wide query row in VGPRs, the whole 512-wide output row in AGPRs). Step t:
+//   1. the score product of tile t+1 (36 products into s_nxt, K from ring slot (t+1) % 3), and
+//      between its products the softmax of tile t on s_cur: mask, maximum, reference, the
+//      numerators 2^(score - m_ref) rounded to bf16 for the PV product, and their exact sum; the
+//      row loads of tile t+2 go out between the first nine products;
+//   2. the PV product of tile t (32 products, V^T from ring slot t % 3, two transposed reads per
+//      V operand, each feeding one product), with the metadata loads of tile t+4 among them (their
+//      address arithmetic costs less here than among the softmax pieces);
+//   3. the wave waits for its row loads of tile t+2, then the workgroup barrier: after it, tile
+//      t+2 is in LDS for every wave, and every wave is done with ring slot t % 3, which the next
+//      step's row loads (tile t+3) refill.
+// No other synchronisation: the waves share the tile ring and nothing else. A vector instruction
+// issued between matrix products runs in the products' shadow only at about two per product (a
+// measured property of gfx950 with one wave per SIMD), so the softmax is spread over the 36 score
+// products a few instructions at a time, each group pinned in place by a scheduling barrier.
 template <bool kWide>
-__device__ __forceinline__ void tile_step(const Ctx& x, int t, int c_begin, const Glob& gl, const Bufs& bf,
-                                          const bf16x8 (&q)[2][kHalfSteps], f32x16 (&oacc)[2][kHalfEBlocks],
-                                          float& m_ref, float& l_lane, bool& over,
-                                          float& best_raw, int& best_col) {
+__device__ __forceinline__ void tile_iter(const Ctx& x_in, int t, int c_begin, const Glob& gl, const Bufs& bf,
+                                          const bf16x8 (&q)[kRegSteps], const int (&k_off)[4], const int (&v_off)[2],
+                                          f32x16 (&oacc)[kEBlocks], f32x16& s_cur, f32x16& s_nxt, RowStats& st) {
   const int tile_c0 = c_begin + t * kTile;
   // The metadata, mask and gather addresses derive from the lane's role; hiding those inputs behind
   // an empty asm makes the compiler rebuild the addresses in each step as short-lived values instead
-  // of keeping a dozen 64-bit addresses live across the whole loop.
-  Ctx xm = x;
-  asm volatile("" : "+v"(xm.lane), "+v"(xm.g), "+v"(xm.my_pair), "+v"(xm.my_half));
-  const uint8_t* __restrict__ kb = bf.kv + (t % kBufs) * kTileBytes;
-  // LDS offsets of this lane's K and V fragments, rebuilt each step from the opaque lane (cheaper
-  // than keeping six more registers live across the loop). K: the lane reads logical chunk
-  // 2ks + g of tile row (lane & 31). V (transposed reads): the 16-lane group G reads tile rows
-  // 16kk + 8m + 4(G/2) + (k16/4), m = 0, 1, latent columns 32eb + 16(G%2) + 4(k16%4) .. +3 of block
-  // eb = 8hf + leb, i.e. logical chunk 4eb + vc with vc = 2(G%2) + (k16%4)/2; the hf part is folded
-  // into the offsets.
-  int k_off[4], v_off0, v_off1;
-#pragma unroll
-  for (int b4 = 0; b4 < 4; ++b4) k_off[b4] = tile_offset(xm.lane & 31, 2 * b4 + xm.g);
-  {
-    const int k16 = xm.lane & 15, G = xm.lane >> 4;
-    const int v_row = 4 * (G >> 1) + (k16 >> 2);
-    const int v_chunk = 2 * (G & 1) + ((k16 & 3) >> 1);
-    v_off0 = tile_offset(v_row, 32 * x.hf + v_chunk) + (k16 & 1) * 8;
-    v_off1 = tile_offset(v_row, 32 * x.hf + 4 + v_chunk) + (k16 & 1) * 8;
-  }
-  const KvGather gat = kv_gather_setup(xm, gl.kv_pool, bf.meta + ((t + 2) % kMetaStages) * kMetaBytes,
-                                       bf.kv + ((t + 2) % kBufs) * kTileBytes);
+  // of hoisting a dozen 64-bit addresses out of the loop (which does not fit the registers).
+  Ctx x = x_in;
+  asm volatile("" : "+v"(x.lane), "+v"(x.g), "+v"(x.my_pair), "+v"(x.my_half));
+  const uint8_t* __restrict__ kb_cur = bf.kv + (t % kBufs) * kTileBytes;
+  const uint8_t* __restrict__ kb_nxt = bf.kv + ((t + 1) % kBufs) * kTileBytes;
+  const uint8_t* meta_cur = bf.meta + (t % kMetaStages) * kMetaBytes;
   uint8_t* const meta_dst = bf.meta + ((t + 4) % kMetaStages) * kMetaBytes;
   const int meta_c0 = tile_c0 + 4 * kTile;
-  // the loads of the step, one after each PV MFMA pair f (the ring buffer they fill is free only
-  // after the step's barrier)
-  auto loads = [&](int f) {
-    switch (f) {  // f is a constant after unrolling
-      case 0: kv_gather_group<kWide, 0>(gat); break;
-      case 1: kv_gather_group<kWide, 1>(gat); break;
-      case 2: kv_gather_group<kWide, 2>(gat); break;
-      case 3: kv_gather_group<kWide, 3>(gat); break;
-      case 4: kv_gather_group<kWide, 4>(gat); break;
-      case 5: kv_gather_group<kWide, 5>(gat); break;
-      case 6: kv_gather_group<kWide, 6>(gat); break;
-      case 7: kv_gather_group<kWide, 7>(gat); break;
-      case 8: kv_gather_group<kWide, 8>(gat); break;
-      case 9: issue_meta_part<0>(xm, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, meta_c0, meta_dst); break;
-      case 11: issue_meta_part<1>(xm, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, meta_c0, meta_dst); break;
-      case 13: issue_meta_part<2>(xm, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, meta_c0, meta_dst); break;
-      default: break;
+  KvGather gat;
+
+  // The LDS reads that feed scalar decisions (this tile's mask byte, the slots of the rows gathered
+  // next) go out before the K operand reads, so the waits for them never drain the reads behind.
+  const int mask_byte = x.uniform_token ? mask_byte_uniform(x, meta_cur) : 0;
+  const u32x4 sb = kv_slot_bytes(x, bf.meta + ((t + 2) % kMetaStages) * kMetaBytes);
+
+  // ---- softmax pieces of tile t (s_cur), spread over the score products of tile t+1
+  uint32_t bits = 0;
+  bool all_vis = false;
+  float raw = -INFINITY;
+  float base = 0.0f;
+  float p_even = 0.0f;
+  bf16x8 pb[2];
+  float psum = 0.0f;
+  // Each piece ends with an empty asm on what it produced: the matrix products are volatile asm too,
+  // so no piece can be moved (by the IR optimiser, which ignores scheduling barriers) away from the
+  // products it is meant to run under.
+  // (fmaxf on values the compiler cannot see the origin of would canonicalise every input first)
+  auto pin = [](float& v) { asm volatile("" : "+v"(v)); };
+  auto max3 = [](float a, float b, float c) {
+    float r;
+    asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+  };
+  auto piece = [&](auto kc) {
+    constexpr int ks = decltype(kc)::value;
+    if constexpr (ks == 0) {
+      bits = x.uniform_token ? mask_word_uniform(x, mask_byte, tile_c0) : mask_word(x, gl.custom_mask, meta_cur, tile_c0);
+      all_vis = __all(bits == 0xFFFFFFFFu);
+    } else if constexpr (ks >= 1 && ks <= 4) {  // element index into the low 4 mantissa bits
+#pragma unroll
+      for (int i = 4 * (ks - 1); i < 4 * ks; ++i)
+        s_cur[i] = __uint_as_float((__float_as_uint(s_cur[i]) & ~15u) | (uint32_t)i);
+      asm volatile("" : "+v"(s_cur));  // in place: the masked branch below then needs no copies
+    } else if constexpr (ks == 5) {
+      if (!all_vis) {  // a tile with hidden columns (draft tiles, arbitrary masks): masked scores are -inf
+        const uint32_t bsh = bits >> (4 * x.g);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s_cur[i] = ((bsh >> (8 * (i >> 2) + (i & 3))) & 1u) ? s_cur[i] : -INFINITY;
+      }
+      asm volatile("" : "+v"(s_cur));
+    } else if constexpr (ks == 6) {
+      raw = max3(max3(s_cur[0], s_cur[1], s_cur[2]), s_cur[3], s_cur[4]);
+    } else if constexpr (ks == 7) {
+      raw = max3(max3(raw, s_cur[5], s_cur[6]), s_cur[7], s_cur[8]);
+    } else if constexpr (ks == 8) {
+      raw = max3(max3(raw, s_cur[9], s_cur[10]), s_cur[11], s_cur[12]);
+    } else if constexpr (ks == 9) {
+      raw = max3(max3(raw, s_cur[13], s_cur[14]), s_cur[15], s_cur[15]);
+      // the lane's best visible score so far and its column (an earlier tile keeps a tie)
+      const int col = (int)(__float_as_uint(raw) & 15u);
+      st.best_col = raw > st.best_raw ? tile_c0 + 8 * (col >> 2) + 4 * x.g + (col & 3) : st.best_col;
+      st.best_raw = fmaxf(st.best_raw, raw);
+    } else if constexpr (ks == 10) {
+      const float mx = pair_max(raw) * x.scale_log2;
+      st.m_ref = st.m_ref == -INFINITY ? mx : st.m_ref;
+      st.over = st.over || mx > st.m_ref + kHeadroom;
+      base = st.m_ref == -INFINITY ? 0.0f : st.m_ref;
+      pin(base);
+    } else if constexpr (ks >= 11 && ks < 27) {  // one numerator per product (2^-inf = 0 when masked)
+      constexpr int i = ks - 11;
+      float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[i], x.scale_log2, -base));
+      pin(pv);
+      if constexpr ((i & 1) == 0) {
+        p_even = pv;
+      } else {
+        const bf16x2 pk = __builtin_convertvector(f32x2{p_even, pv}, bf16x2);
+        pb[i >> 3][(i - 1) & 7] = pk[0];
+        pb[i >> 3][i & 7] = pk[1];
+        psum += p_even + pv;
+      }
+    } else if constexpr (ks == 27) {
+      st.l_lane += psum;
     }
   };
 
-  // 1. S^T = K . Q^T for the own block (s_own), one k-step at a time; fragment ks is logical chunk
-  // 2ks + g of row (lane & 31), at k_off[ks % 4] + 1024 (ks / 4), read kKAhead k-steps ahead; query
-  // k-step ks is q[ks / 18][ks % 18].
-  f32x16 s_own = {};
-  uint32_t bits;
-  {
-    constexpr int kKAhead = 3;
-    constexpr int kSteps = 2 * kHalfSteps;  // 36 k-steps over the whole 576-wide row
-    bf16x8 kf[kKAhead + 1];
-    auto load_k = [&](int ks) {
-      kf[ks % (kKAhead + 1)] = *reinterpret_cast<const bf16x8*>(kb + k_off[ks % 4] + kGroupBytes * (ks / 4));
-    };
+  // ---- 1. score product of tile t+1 with the softmax of tile t between its products (the LDS reads
+  // of the mask byte and of the gathered rows' slots went out first, see above)
+  constexpr int kKAhead = 2;
+  bf16x8 kf[kKAhead + 1];
 #pragma unroll
-    for (int ks = 0; ks < kKAhead; ++ks) load_k(ks);
-#pragma unroll
-    for (int ks = 0; ks < kSteps; ++ks) {
-      if (ks + kKAhead < kSteps) load_k(ks + kKAhead);
-      __builtin_amdgcn_sched_barrier(0);
-      s_own = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks % (kKAhead + 1)], q[ks / kHalfSteps][ks % kHalfSteps],
-                                                      s_own, 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+  for (int ks = 0; ks < kKAhead; ++ks) kf[ks] = load_k(kb_nxt, k_off, ks);
+  piece(std::integral_constant<int, 0>{});  // the first mask and index work covers the first K reads' latency
+  gat = kv_gather_build(x, gl.kv_pool, sb, bf.kv + ((t + 2) % kBufs) * kTileBytes);
+  __builtin_amdgcn_sched_barrier(0);
+  bf16x8 qr[kSteps - kRegSteps];  // rope query operands, read from LDS kKAhead k-steps ahead
+  static_for<0, kSteps>([&](auto kc) {
+    constexpr int ks = decltype(kc)::value;
+    if constexpr (ks + kKAhead < kSteps) {
+      kf[(ks + kKAhead) % (kKAhead + 1)] = load_k(kb_nxt, k_off, ks + kKAhead);
+      if constexpr (ks + kKAhead >= kRegSteps) qr[ks + kKAhead - kRegSteps] = q_operand<ks + kKAhead>(q, bf, x.lane);
     }
-    bits = mask_word(xm, gl.custom_mask, bf.meta + (t % kMetaStages) * kMetaBytes, tile_c0);
-  }
+    if constexpr (ks == 0)
+      qk_first(s_nxt, kf[0], q[0]);
+    else if constexpr (ks < kRegSteps)
+      qk_next(s_nxt, kf[ks % (kKAhead + 1)], q[ks]);
+    else
+      qk_next(s_nxt, kf[ks % (kKAhead + 1)], qr[ks - kRegSteps]);
+    if constexpr (ks + 1 < 28) piece(std::integral_constant<int, ks + 1>{});
+    // the row loads of tile t+2, one after each of the first nine products: they need most of the
+    // step to land (a CU's gathers of one tile complete about 3000 cycles after the first is issued,
+    // wherever in the step they go; nine back to back before the first product cost more issue time)
+    if constexpr (ks >= 0 && ks <= 8) kv_gather_group<kWide, ks>(gat);
 
-  // 2. mask + softmax numerators against the row's reference max m_ref (base-2 units of the scaled
-  // score). The reference is the max of the first tile with a visible column and then stays fixed,
-  // so the accumulators are never rescaled; a later score above m_ref + kHeadroom raises `over`,
-  // and the kernel then reruns the split with m_ref = the row's true max. Element i of s_own is
-  // column 8(i/4) + 4g + i%4 of the tile; bit c of `bits` marks column c visible for this lane's row.
-  // The low 4 mantissa bits of each score are replaced by its element index (a change of at most
-  // 15 ulp, far below the bf16 rounding of the probabilities), so the max below also names its
-  // element and every score is distinct within the lane.
-#pragma unroll
-  for (int i = 0; i < 16; ++i) s_own[i] = __uint_as_float((__float_as_uint(s_own[i]) & ~15u) | (uint32_t)i);
-  float raw = -INFINITY;  // max of the visible raw dot products (scale > 0)
-  if (__all(bits == 0xFFFFFFFFu)) {  // every column visible for every row (prefix tiles)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) raw = fmaxf(raw, s_own[i]);
-  } else {
-    const uint32_t bsh = bits >> (4 * x.g);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      s_own[i] = ((bsh >> (8 * (i >> 2) + (i & 3))) & 1u) ? s_own[i] : -INFINITY;
-      raw = fmaxf(raw, s_own[i]);
-    }
-  }
-  // the lane's largest visible score so far and its column (the index rides in the score's low
-  // bits; an earlier tile keeps a tie): the row's largest probability is put back at its exact
-  // value when the split ends
-  {
-    const int col = (int)(__float_as_uint(raw) & 15u);
-    best_col = raw > best_raw ? tile_c0 + 8 * (col >> 2) + 4 * x.g + (col & 3) : best_col;
-    best_raw = fmaxf(best_raw, raw);
-  }
-  const float mx = pair_max(raw) * x.scale_log2;
-  m_ref = m_ref == -INFINITY ? mx : m_ref;
-  over = over || mx > m_ref + kHeadroom;
-  const float base = m_ref == -INFINITY ? 0.0f : m_ref;
-  bf16x8 pb_own[2];
-  float psum = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; i += 2) {
-    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_own[i], x.scale_log2, -base));  // 2^-inf = 0
-    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_own[i + 1], x.scale_log2, -base));
-    const bf16x2 pk = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
-    psum += p0 + p1;
-    pb_own[i >> 3][i & 7] = pk[0];
-    pb_own[i >> 3][(i & 7) + 1] = pk[1];
-  }
-  l_lane += psum;
+    __builtin_amdgcn_sched_barrier(0);
+  });
 
-  // 3. probability exchange inside the pair
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) *reinterpret_cast<bf16x8*>(bf.p_mine + (t & 1) * kPXchgBytes + kk * 1024) = pb_own[kk];
-  // this wave's row loads of tile t+1 (issued in the previous step's PV phase) have landed; after
-  // the barrier every wave's have, so the next step needs no barrier of its own
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  bf16x8 pb_oth[2];
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-    pb_oth[kk] = *reinterpret_cast<const bf16x8*>(bf.p_other + (t & 1) * kPXchgBytes + kk * 1024);
-
-  // 4. O^T[e half] += V^T . P^T for both blocks; k-step kk covers tile columns [16kk, 16kk+16)
-  // permuted as logical k = 8g + j  <->  column 16kk + 4g + j (j < 4), 16kk + 8 + 4g + (j - 4)
-  // (j >= 4). V fragment f = (kk, leb) = (f / 8, f % 8) is read kVAhead fragments ahead with two
-  // transposed reads and feeds the MFMAs of both blocks.
+  // ---- 2. PV product of tile t: O^T[eb] += V^T(kk, eb) . P^T(kk); V operands two ahead
   constexpr int kVAhead = 2;
   bf16x8 vf[kVAhead + 1];
-  auto load_v = [&](int f) {
-    const int kk = f >> 3, leb = f & 7;  // leb: block of 32 output columns inside this wave's half
-    // rows 16kk + 8m + v_row (regions 2kk + m), latent chunk 4(8hf + leb) + v_chunk
-    const uint8_t* p0 = kb + (leb & 1 ? v_off1 : v_off0) + 2 * kk * kRegionBytes + kGroupBytes * (leb >> 1);
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + kRegionBytes));
-    vf[f % (kVAhead + 1)] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-  };
 #pragma unroll
-  for (int f = 0; f < kVAhead; ++f) load_v(f);
-#pragma unroll
-  for (int f = 0; f < 2 * kHalfEBlocks; ++f) {
-    if (f + kVAhead < 2 * kHalfEBlocks) load_v(f + kVAhead);
+  for (int f = 0; f < kVAhead; ++f) vf[f] = load_v(kb_cur, v_off, f >> 4, f & 15);
+  static_for<0, 2 * kEBlocks>([&](auto fc) {
+    constexpr int f = decltype(fc)::value;
+    if constexpr (f + kVAhead < 2 * kEBlocks)
+      vf[(f + kVAhead) % (kVAhead + 1)] = load_v(kb_cur, v_off, (f + kVAhead) >> 4, (f + kVAhead) & 15);
     __builtin_amdgcn_sched_barrier(0);
-    const int kk = f >> 3, leb = f & 7;
-    oacc[0][leb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[f % (kVAhead + 1)], pb_own[kk], oacc[0][leb], 0, 0, 0);
+    oacc[f & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[f % (kVAhead + 1)], pb[f >> 4], oacc[f & 15], 0, 0, 0);
+    if constexpr (f == 4) issue_meta_part<0>(x, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, meta_c0, meta_dst);
+    if constexpr (f == 8) issue_meta_part<1>(x, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, meta_c0, meta_dst);
+    if constexpr (f == 12) issue_meta_part<2>(x, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, meta_c0, meta_dst);
     __builtin_amdgcn_sched_barrier(0);
-    oacc[1][leb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[f % (kVAhead + 1)], pb_oth[kk], oacc[1][leb], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    loads(f);
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  });
+
+  // ---- 3. this wave's row loads of tile t+2 have landed (the metadata loads issued after them may
+  // still be in flight: loads retire in order), then the barrier
+  if (x.n_meta == 1)
+    __builtin_amdgcn_s_waitcnt(1 | (0x7 << 4) | (0xF << 8));
+  else if (x.n_meta == 2)
+    __builtin_amdgcn_s_waitcnt(2 | (0x7 << 4) | (0xF << 8));
+  else
+    __builtin_amdgcn_s_waitcnt(3 | (0x7 << 4) | (0xF << 8));
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // The score block of tile t+1 stays allocated to the end of the step. The compiler takes an asm
+  // product as finished when it is issued, but the matrix core writes its result some 30 cycles
+  // later; in the last step, where that block is never read, the compiler would otherwise hand its
+  // registers to the PV phase's addresses and operands right after the last product, and the late
+  // write would clobber them.
+  asm volatile("" : "+v"(s_nxt));
 }
 
-// Partial kernel. Wave pair p owns 64 query rows in two blocks of 32; its wave h (0/1) holds the
-// whole query rows of block h and, for both blocks, the output columns e in [256h, 256h + 256).
-// Per 32-column tile each wave scores and softmaxes its own block, the pair swaps the bf16
-// probabilities through LDS, and each wave updates its output half of both blocks.
+// Partial kernel body. Wave w owns query rows 32w .. 32w+31 of the row tile: it scores them against
+// every column of the split, runs their softmax and accumulates their 512-wide outputs; the four
+// waves share only the ring of KV tiles they gather together.
 //
 // Vector-memory pipeline: everything a tile needs arrives through direct-to-LDS loads, so no loaded
 // register is waited on inside the loop. Step t issues the 9 row loads of tile t+2 and the n_meta
-// metadata loads of tile t+4; each wave waits for all of its loads before the probability-exchange
-// barrier of every step, so tile t+1 (and the metadata of tile t+3) are in LDS for everyone after
-// it. Before the first step the prologue has issued tiles 0 and 1 and the metadata of tiles 0-3;
-// loads retire in order, so "at most 9 + n_meta outstanding" then means tile 0 and the metadata of
-// tile 2 have landed, and one barrier publishes them.
+// metadata loads of tile t+4 and waits for the row loads before its barrier, so tile t+2 (and, in
+// order, the metadata of tile t+3) is in LDS for everyone after it. The prologue issues the metadata
+// of tiles 0-3 and the rows of tiles 0 and 1, waits for both tiles and scores tile 0.
 // Prefetches past the split read clamped, valid addresses into buffers that are never read.
 // Inputs of the partial kernels that every split reads.
 struct PartialArgs {
@@ -516,8 +584,8 @@ struct PartialArgs {
 // The partial kernels' LDS.
 struct PartialLds {
   uint8_t* kv;
-  uint8_t* p;
   uint8_t* meta;
+  uint8_t* q_rope;
   int* over;
 };
 
@@ -537,37 +605,32 @@ __device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds
   const int H = a.H, q_len = a.q_len;
   const int lane = threadIdx.x & 63;
   const int w = wave_uniform(threadIdx.x >> 6);
-  const int pr_id = w >> 1, hf = w & 1;
   const int R = q_len * H;
   const int kv_start = a.kv_indptr[b];
   const int P = max(a.kv_indptr[b + 1] - kv_start, 0);
   const int L = P + q_len;
 
   const int g = lane >> 5;  // k-group of the MFMA operands
-  const int pair_row0 = rt * kRowsPerWG + pr_id * kRowsPerPair;
-  // register set i of this wave holds row block i ^ hf of the pair: set 0 is the own block
-  auto set_row = [&](int i) { return pair_row0 + kBlockRows * (i ^ hf) + (lane & 31); };
-  const int own_row0 = pair_row0 + kBlockRows * hf;
-  const int own_row = set_row(0);
+  const int own_row0 = rt * kRowsPerWG + w * kBlockRows;
+  const int own_row = own_row0 + (lane & 31);
   if (c_begin >= c_end) {
     if (own_row < R && g == 0) ws_ml[part + own_row] = make_float2(-INFINITY, 0.0f);
     return;
   }
 
-  // ---- this wave's half of both blocks' query rows as MFMA B operands: k-step ks of set i holds
-  // Q[row][288 hf + 16 ks + 8 g .. +8] (rows past R load row R-1 and are zeroed)
-  bf16x8 q[2][kHalfSteps];
+  // ---- the wave's query rows as MFMA B operands: k-step ks holds Q[row][16 ks + 8 g .. +8] (rows
+  // past R load row R-1 and are zeroed)
+  bf16x8 q[kRegSteps];
+  uint8_t* const q_lds = lds.q_rope + w * kQRopeBytes;
   {
-    const int row = own_row;
-    const int q_row = min(row, R - 1);
+    const int q_row = min(own_row, R - 1);
     const bf16x8* qn = reinterpret_cast<const bf16x8*>(q_nope + ((size_t)b * R + q_row) * kLatent);
     const bf16x8* qr = reinterpret_cast<const bf16x8*>(q_rope + ((size_t)b * R + q_row) * kRope);
 #pragma unroll
-    for (int ks = 0; ks < 2 * kHalfSteps; ++ks) {
-      const int chunk8 = 2 * ks + g;  // 8-value chunk of the 576-wide row
-      const bf16x8 v = chunk8 < kLatent / 8 ? qn[chunk8] : qr[chunk8 - kLatent / 8];
-      q[ks / kHalfSteps][ks % kHalfSteps] = row < R ? v : bf16x8{};
-    }
+    for (int ks = 0; ks < kRegSteps; ++ks) q[ks] = own_row < R ? qn[2 * ks + g] : bf16x8{};
+#pragma unroll
+    for (int j = 0; j < kSteps - kRegSteps; ++j)  // rope k-steps to LDS (read after the prologue barrier)
+      *reinterpret_cast<bf16x8*>(q_lds + 1024 * j + 16 * lane) = own_row < R ? qr[2 * j + g] : bf16x8{};
   }
 
   Ctx x;
@@ -581,11 +644,11 @@ __device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds
   x.c_end = c_end;
   x.lane = lane;
   x.g = g;
-  x.hf = hf;
   x.loader_row0 = (w % kLoaders) * kRowsPerLoader;
-  // tokens of the own block's rows (a block past R uses the last token: valid, never stored)
+  // tokens of the wave's rows (a block past R uses the last token: valid, never stored)
   x.tok_first = min(own_row0, R - 1) / H;
   x.tok_last = (min(own_row0 + kBlockRows, R) - 1) / H;
+  x.uniform_token = x.tok_first == x.tok_last;
   const int my_tok_ix = min(own_row, R - 1) / H - x.tok_first;
   x.my_pair = my_tok_ix >> 1;
   x.my_half = my_tok_ix & 1;
@@ -595,86 +658,116 @@ __device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds
   x.scale_log2 = a.scale_log2;
   uint8_t* const meta = lds.meta + w * kMetaStages * kMetaBytes;
   uint8_t* const lds_kv = lds.kv;
-  const Bufs bf = {lds_kv, meta, lds.p + w * 2 * kPXchgBytes + lane * 16,
-                   lds.p + (w ^ 1) * 2 * kPXchgBytes + lane * 16};
+  const Bufs bf = {lds_kv, meta, q_lds};
   const Glob gl = {kv_pool, kv_indices, out_cache_loc, custom_mask};
 
+  // per-lane LDS offsets inside a tile, the same for every tile. K: logical chunk 2 b4 + g of tile row
+  // lane & 31 (k-step ks uses b4 = ks % 4 plus 1024 (ks / 4)). V (transposed reads): the 16-lane
+  // group G reads tile rows 16kk + 8m + 4(G/2) + (k16/4), m = 0, 1, latent columns 32eb + 16(G%2) +
+  // 4(k16%4) .. +3, i.e. logical chunk 4eb + vc with vc = 2(G%2) + (k16%4)/2; v_off[eb % 2] plus
+  // 1024 (eb / 2) and the region offsets of rows 16kk + 8m.
+  int k_off[4], v_off[2];
+#pragma unroll
+  for (int b4 = 0; b4 < 4; ++b4) k_off[b4] = tile_offset(lane & 31, 2 * b4 + g);
+  {
+    const int k16 = lane & 15, G = lane >> 4;
+    const int v_row = 4 * (G >> 1) + (k16 >> 2);
+    const int v_chunk = 2 * (G & 1) + ((k16 & 3) >> 1);
+    v_off[0] = tile_offset(v_row, v_chunk) + (k16 & 1) * 8;
+    v_off[1] = tile_offset(v_row, 4 + v_chunk) + (k16 & 1) * 8;
+  }
+
   const int ntiles = (c_end - c_begin + kTile - 1) / kTile;
-  f32x16 oacc[2][kHalfEBlocks];
-  float m_ref = -INFINITY;   // reference max of the own row (base-2 units), fixed once set
-  float l_lane = 0.0f;
-  // the lane's largest visible raw score of the split (index bits included) and its column
-  float best_raw = -INFINITY;
-  int best_col = 0;
+  f32x16 oacc[kEBlocks];
+  RowStats st;
+  st.m_ref = -INFINITY;
   int* const lds_over = lds.over;
 
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int eb = 0; eb < kHalfEBlocks; ++eb) oacc[i][eb] = f32x16{};
-    l_lane = 0.0f;
-    best_raw = -INFINITY;
-    best_col = 0;
-    bool over = false;
+    for (int eb = 0; eb < kEBlocks; ++eb) oacc[eb] = f32x16{};
+    const float m_fixed = st.m_ref;  // pass 1: each row's true max over the split (set below)
+    st.m_ref = pass == 0 ? -INFINITY : m_fixed;
+    st.l_lane = 0.0f;
+    st.best_raw = -INFINITY;
+    st.best_col = 0;
+    st.over = false;
 
-    // ---- prologue, laid out like the steady state: ... rows(t+1), meta(t+3), rows(t+2), meta(t+4) ...
+    // ---- prologue: metadata of tiles 0-3, rows of tiles 0 and 1, then the scores of tile 0
     issue_meta(x, kv_indices, out_cache_loc, custom_mask, c_begin, meta);
     issue_meta(x, kv_indices, out_cache_loc, custom_mask, c_begin + kTile, meta + kMetaBytes);
     __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0): query rows and metadata
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int ks = 0; ks < kHalfSteps; ++ks) asm volatile("" ::"v"(q[i][ks]));  // query rows ready here
+    for (int ks = 0; ks < kRegSteps; ++ks) asm volatile("" ::"v"(q[ks]));  // query rows ready here
     issue_kv<kWide>(x, kv_pool, meta, lds_kv);
     issue_meta(x, kv_indices, out_cache_loc, custom_mask, c_begin + 2 * kTile, meta + 2 * kMetaBytes);
     issue_kv<kWide>(x, kv_pool, meta + kMetaBytes, lds_kv + kTileBytes);
     issue_meta(x, kv_indices, out_cache_loc, custom_mask, c_begin + 3 * kTile, meta + 3 * kMetaBytes);
-
-    // tile 0 and the metadata of tile 2 have landed (tile 1 may still be in flight)
-    static_assert(kLoadsPerWave + kMetaExtra + 1 < 16, "vmcnt immediate");
+    // tiles 0 and 1 have landed (the metadata of tile 3 may still be in flight)
+    static_assert(kMetaExtra + 1 < 16, "vmcnt immediate");
     if (x.n_meta == 1)
-      __builtin_amdgcn_s_waitcnt((kLoadsPerWave + 1) | (0x7 << 4) | (0xF << 8));
+      __builtin_amdgcn_s_waitcnt(1 | (0x7 << 4) | (0xF << 8));
     else if (x.n_meta == 2)
-      __builtin_amdgcn_s_waitcnt((kLoadsPerWave + 2) | (0x7 << 4) | (0xF << 8));
+      __builtin_amdgcn_s_waitcnt(2 | (0x7 << 4) | (0xF << 8));
     else
-      __builtin_amdgcn_s_waitcnt((kLoadsPerWave + 3) | (0x7 << 4) | (0xF << 8));
+      __builtin_amdgcn_s_waitcnt(3 | (0x7 << 4) | (0xF << 8));
     lds_barrier();
-    for (int t = 0; t < ntiles; ++t)
-      tile_step<kWide>(x, t, c_begin, gl, bf, q, oacc, m_ref, l_lane, over, best_raw, best_col);
-    // the last iterations prefetched rows past the split; let them land before LDS is reused
+    f32x16 s_a, s_b;
+    {
+      bf16x8 kf[4];
+#pragma unroll
+      for (int ks = 0; ks < 3; ++ks) kf[ks] = load_k(lds_kv, k_off, ks);
+      static_for<0, kSteps>([&](auto kc) {
+        constexpr int ks = decltype(kc)::value;
+        if constexpr (ks + 3 < kSteps) kf[(ks + 3) % 4] = load_k(lds_kv, k_off, ks + 3);
+        if constexpr (ks == 0)
+          qk_first(s_a, kf[0], q[0]);
+        else
+          qk_next(s_a, kf[ks % 4], q_operand<ks>(q, bf, lane));
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      qk_settle(s_a);
+    }
+    // ---- the tile loop, two steps per trip so the two score blocks trade roles without copies
+    int t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+      tile_iter<kWide>(x, t, c_begin, gl, bf, q, k_off, v_off, oacc, s_a, s_b, st);
+      tile_iter<kWide>(x, t + 1, c_begin, gl, bf, q, k_off, v_off, oacc, s_b, s_a, st);
+    }
+    if (t < ntiles) tile_iter<kWide>(x, t, c_begin, gl, bf, q, k_off, v_off, oacc, s_a, s_b, st);
+    // the last steps prefetched rows past the split; let them land before LDS is reused
     __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0)
 
     // a score above its row's reference + headroom anywhere in the workgroup: rerun the split
     // with every row's reference at its true max (the second pass cannot overflow)
-    if (lane == 0) lds_over[w] = __any(over) ? 1 : 0;
+    if (lane == 0) lds_over[w] = __any(st.over) ? 1 : 0;
     lds_barrier();
     int any_over = 0;
 #pragma unroll
     for (int k = 0; k < kWaves; ++k) any_over |= lds_over[k];
     lds_barrier();
     if (!any_over) break;
-    m_ref = pair_max(best_raw) * x.scale_log2;  // the row's true max over the split
+    st.m_ref = pair_max(st.best_raw) * x.scale_log2;  // the row's true max over the split
   }
 
   // ---- the row's top probability. Each visible column entered the PV product with its probability
   // rounded to bf16 (the sum l took the exact values). For the row's largest one (the same fma +
   // exp2 as in the tile, so the same value) the exact probability and the pool slot of its value
-  // row go to the top record; the combine adds back what the rounding dropped, (p - bf16(p)) times that
-  // value row, where the column matters against the row's final sum. Without that, a row dominated
-  // by one column whose score came after the reference tile is off by up to 2^-9 of that column's
-  // values. The lane pair first agrees on the row's best column.
+  // row go to the top record; the combine adds back what the rounding dropped, (p - bf16(p)) times
+  // that value row, where the column matters against the row's final sum. Without that, a row
+  // dominated by one column whose score came after the reference tile is off by up to 2^-9 of that
+  // column's values. The lane pair first agrees on the row's best column.
   {
-    const auto rs = __builtin_amdgcn_permlane32_swap(__float_as_uint(best_raw), __float_as_uint(best_raw), false,
-                                                     false);
-    const auto cs = __builtin_amdgcn_permlane32_swap((unsigned)best_col, (unsigned)best_col, false, false);
+    const auto rs = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.best_raw), __float_as_uint(st.best_raw),
+                                                     false, false);
+    const auto cs = __builtin_amdgcn_permlane32_swap((unsigned)st.best_col, (unsigned)st.best_col, false, false);
     const float ra = __uint_as_float(rs[0]), rb = __uint_as_float(rs[1]);
     const int ca = (int)cs[0], cb = (int)cs[1];
     const bool take_b = rb > ra || (rb == ra && cb < ca);
     const float top = take_b ? rb : ra;
     const int col = take_b ? cb : ca;
     if (own_row < R && g == 0) {
-      const float base = m_ref == -INFINITY ? 0.0f : m_ref;
+      const float base = st.m_ref == -INFINITY ? 0.0f : st.m_ref;
       const float p = top == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(__builtin_fmaf(top, x.scale_log2, -base));
       int slot = col < P ? kv_indices[kv_start + col] : out_cache_loc[(size_t)b * q_len + (col - P)];
       slot = min(max(slot, 0), a.N - 1);
@@ -682,33 +775,28 @@ __device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds
     }
   }
 
-  // ---- partial write: (m_ref, l) of the own block and this wave's half of both blocks'
-  // unnormalised accumulators
-  const float l_row = pair_sum(l_lane);
+  // ---- partial write: (m_ref, l) and the unnormalised 512-wide accumulator of the wave's rows
+  const float l_row = pair_sum(st.l_lane);
+  if (own_row < R) {
+    float* dst = ws_acc + (part + own_row) * kLatent;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = set_row(i);
-    if (row < R) {
-      float* dst = ws_acc + (part + row) * kLatent + 256 * hf;
+    for (int eb = 0; eb < kEBlocks; ++eb) {
 #pragma unroll
-      for (int eb = 0; eb < kHalfEBlocks; ++eb) {
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const f32x4 val = {oacc[i][eb][4 * a], oacc[i][eb][4 * a + 1], oacc[i][eb][4 * a + 2], oacc[i][eb][4 * a + 3]};
-          *reinterpret_cast<f32x4*>(dst + 32 * eb + 8 * a + 4 * g) = val;
-        }
+      for (int k = 0; k < 4; ++k) {
+        const f32x4 val = {oacc[eb][4 * k], oacc[eb][4 * k + 1], oacc[eb][4 * k + 2], oacc[eb][4 * k + 3]};
+        *reinterpret_cast<f32x4*>(dst + 32 * eb + 8 * k + 4 * g) = val;
       }
     }
   }
-  if (own_row < R && g == 0) ws_ml[part + own_row] = make_float2(m_ref, l_row);
+  if (own_row < R && g == 0) ws_ml[part + own_row] = make_float2(st.m_ref, l_row);
 }
 
 #define PARTIAL_LDS_DECL                                                          \
   __shared__ __attribute__((aligned(16))) uint8_t lds_kv[kBufs * kTileBytes];     \
-  __shared__ __attribute__((aligned(16))) uint8_t lds_p[kWaves * 2 * kPXchgBytes];\
   __shared__ __attribute__((aligned(16))) uint8_t lds_meta[kWaves * kMetaStages * kMetaBytes]; \
+  __shared__ __attribute__((aligned(16))) uint8_t lds_qrope[kWaves * kQRopeBytes]; \
   __shared__ int lds_over[kWaves];                                                \
-  const PartialLds lds = {lds_kv, lds_p, lds_meta, lds_over};
+  const PartialLds lds = {lds_kv, lds_meta, lds_qrope, lds_over};
 
 // Per-request splits: workgroup -> (request b, split s, row tile) by decode_unit; split s of request
 // b covers columns [s*chunk, min(L_b, (s+1)*chunk)) with chunk = ceil(L_b / nsplit) rounded up to the

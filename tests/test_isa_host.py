@@ -66,3 +66,43 @@ def test_partial_kernels_do_not_use_scratch_inside_the_tile_loop(device_asm):
         assert len(mfma) >= 68
         loop = body[mfma[0]:mfma[-1]]
         assert "scratch_" not in loop, f"scratch access inside the tile loop of {m.group(1)[:60]}"
+
+
+def _vgprs(op):
+    m = re.fullmatch(r"[va]\[(\d+):(\d+)\]", op)
+    if m:
+        return (op[0], set(range(int(m.group(1)), int(m.group(2)) + 1)))
+    m = re.fullmatch(r"([va])(\d+)", op)
+    return (m.group(1), {int(m.group(2))}) if m else None
+
+
+def test_asm_products_settle_before_their_registers_are_touched(device_asm):
+    """The score products are inline asm, so the compiler takes each as finished once issued and
+    inserts no wait states after it; the matrix core writes the 16 result registers some 30 cycles
+    later. Any other instruction that reads or writes those registers before the product chain has
+    settled sees (or is overwritten by) the late result. This proves, for every product with a VGPR
+    result, that the next instruction touching its registers is either the chain's next product
+    (same registers as accumulator, which the matrix core forwards) or comes at least 24 issue slots
+    later (3 x s_nop 7, as qk_settle gives; an s_nop N counts N + 1, any other instruction 1)."""
+    ins = _instructions(device_asm)
+    checked = 0
+    for i, l in enumerate(ins):
+        parts = re.split(r"[\s,]+", l)
+        if not parts[0].startswith("v_mfma") or not parts[1].startswith("v["):
+            continue
+        dst = _vgprs(parts[1])
+        slots = 0
+        for j in range(i + 1, len(ins)):
+            p = re.split(r"[\s,]+", ins[j])
+            ops = [_vgprs(o) for o in p[1:]]
+            if p[0].startswith("v_mfma") and ops[0] == dst and len(ops) > 3 and ops[3] == dst:
+                break  # the chain's next product
+            if any(o and o[0] == dst[0] and o[1] & dst[1] for o in ops):
+                assert slots >= 24, f"{ins[j]} touches the result of {l} {slots} slots after it"
+                break
+            if slots >= 24:
+                break
+            m = re.fullmatch(r"s_nop (\d+)", ins[j])
+            slots += int(m.group(1)) + 1 if m else 1
+        checked += 1
+    assert checked > 0
