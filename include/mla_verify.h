@@ -23,14 +23,15 @@
  *
  * Conventions for every entry point:
  *  - Device pointers refer to memory of the current HIP device; host scalars are passed by value.
- *  - The caller owns every buffer. The library never allocates, frees, copies through the host
- *    or synchronises; it only enqueues kernels on `stream` (NULL = the default stream).
+ *  - The caller owns every buffer (the no-alloc call's static scratch aside). The library never
+ *    allocates, frees, copies through the host or synchronises; it only enqueues kernels on
+ *    `stream` (NULL = the default stream).
  *  - Argument errors are detected on the host and returned as a negative status before any HIP
  *    call is made. A failed kernel launch returns MLA_VERIFY_ERR_LAUNCH.
  *  - The call is asynchronous and can be captured into a hipGraph: the launch configuration
  *    depends only on (B, q_len, H, nsplit), and every length is read on the device.
- *  - There is no global mutable state: calls on different streams with different workspaces
- *    may run concurrently.
+ *  - Apart from the static scratch of mla_verify_attn_balanced_noalloc there is no global mutable
+ *    state: calls on different streams with different workspaces may run concurrently.
  */
 #ifndef MLA_VERIFY_H
 #define MLA_VERIFY_H
@@ -50,7 +51,8 @@ typedef enum {
     MLA_VERIFY_ERR_SHAPE = -2,     /* B, q_len, H or N out of range, or scale not finite and > 0 */
     MLA_VERIFY_ERR_NSPLIT = -3,    /* nsplit outside [1, MLA_VERIFY_MAX_NSPLIT] */
     MLA_VERIFY_ERR_WORKSPACE = -4, /* workspace NULL, misaligned or smaller than required */
-    MLA_VERIFY_ERR_LAUNCH = -5     /* the HIP runtime refused a kernel launch */
+    MLA_VERIFY_ERR_LAUNCH = -5,    /* the HIP runtime refused a kernel launch */
+    MLA_VERIFY_ERR_SCRATCH = -6    /* the sizes need more than the static scratch of the no-alloc call */
 } mla_verify_status;
 
 #define MLA_VERIFY_LATENT 512          /* latent (value) width of a KV row */
@@ -60,6 +62,7 @@ typedef enum {
 #define MLA_VERIFY_WORKSPACE_ALIGN 256 /* required alignment of the workspace pointer */
 #define MLA_VERIFY_MAX_UNITS 4096      /* largest `units` of the balanced entry points */
 #define MLA_VERIFY_BALANCED_MAX_B 4096 /* largest B of the balanced entry points */
+#define MLA_VERIFY_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20) /* static scratch per device (no-alloc call) */
 
 /*
  * Bytes of workspace mla_verify_attn needs for these sizes ("From Capture Safety to MoE
@@ -204,6 +207,31 @@ int mla_verify_attn_balanced_partial(const void *q_nope, const void *q_rope, con
 int mla_verify_attn_balanced_combine(const void *workspace, size_t workspace_bytes, const void *kv_pool,
                                      int64_t N, int B, int q_len, int H, int units, void *out, float *lse,
                                      hipStream_t stream);
+
+/*
+ * mla_verify_attn_balanced without a workspace argument, for callers that cannot allocate device
+ * memory: code under hipGraph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments, rules and result as mla_verify_attn_balanced (the same kernels run), with the
+ * workspace taken from a static device array of MLA_VERIFY_NOALLOC_SCRATCH_BYTES (128 MiB) that the
+ * library defines. Every device the library's code is loaded on holds its own copy of that array
+ * until the process ends. The first call on a device (the current one) resolves the array's address
+ * there, once, and keeps it; no call allocates, frees or copies memory. Nothing in the array needs
+ * initialising: each call rewrites the plan and the partials it reads.
+ *
+ * Sizes whose balanced workspace (mla_verify_attn_balanced_workspace_size) exceeds the array return
+ * MLA_VERIFY_ERR_SCRATCH before any HIP call; a device whose copy of the array cannot be resolved
+ * returns MLA_VERIFY_ERR_LAUNCH.
+ *
+ * All calls on one device share that device's array: two calls whose kernels can overlap (on
+ * different streams, or on one stream while a graph containing another such call runs) race on it
+ * and their results are undefined. Order them on one stream or synchronise in between.
+ */
+int mla_verify_attn_balanced_noalloc(const void *q_nope, const void *q_rope, const void *kv_pool, int64_t N,
+                                     const int32_t *kv_indptr, const int32_t *kv_indices,
+                                     const int32_t *out_cache_loc, const uint8_t *custom_mask,
+                                     const int32_t *mask_indptr, int B, int q_len, int H, float scale,
+                                     int units, void *out, float *lse, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -14,9 +14,11 @@ LIB_PATH = os.path.join(_PKG, "libmla_verify.so")
 LATENT, ROPE, ROW = 512, 64, 576
 MAX_NSPLIT = 1024
 WORKSPACE_ALIGN = 256
+NOALLOC_SCRATCH_BYTES = 128 << 20  # static scratch per device of the no-alloc entry point
 
 STATUS = {0: "MLA_VERIFY_OK", -1: "MLA_VERIFY_ERR_NULL", -2: "MLA_VERIFY_ERR_SHAPE",
-          -3: "MLA_VERIFY_ERR_NSPLIT", -4: "MLA_VERIFY_ERR_WORKSPACE", -5: "MLA_VERIFY_ERR_LAUNCH"}
+          -3: "MLA_VERIFY_ERR_NSPLIT", -4: "MLA_VERIFY_ERR_WORKSPACE", -5: "MLA_VERIFY_ERR_LAUNCH",
+          -6: "MLA_VERIFY_ERR_SCRATCH"}
 
 _lib = None
 
@@ -55,6 +57,8 @@ def library() -> ctypes.CDLL:
         lib.mla_verify_attn_balanced_partial.restype = i32
         lib.mla_verify_attn_balanced_combine.argtypes = lib.mla_verify_attn_combine.argtypes
         lib.mla_verify_attn_balanced_combine.restype = i32
+        lib.mla_verify_attn_balanced_noalloc.argtypes = lib.mla_verify_attn.argtypes[:14] + [vp, vp, vp]
+        lib.mla_verify_attn_balanced_noalloc.restype = i32
         lib.mla_verify_attn_check.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp, i32, vp,
                                               sz, vp, vp]
         lib.mla_verify_attn_check_workspace_size.argtypes = [i32, i32, i32, i32]
@@ -130,6 +134,16 @@ def balanced_combine_raw(workspace, workspace_bytes, kv_pool, N, B, q_len, H, un
     """Direct call of mla_verify_attn_balanced_combine; returns the status."""
     return int(library().mla_verify_attn_balanced_combine(workspace, int(workspace_bytes), kv_pool, int(N), int(B),
                                                           int(q_len), int(H), int(units), out, lse, stream))
+
+
+def balanced_noalloc_raw(q_nope, q_rope, kv_pool, N, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
+                         B, q_len, H, scale, units, out, lse, stream) -> int:
+    """Direct call of mla_verify_attn_balanced_noalloc (the library's static scratch in place of a
+    workspace); returns the status."""
+    return int(library().mla_verify_attn_balanced_noalloc(q_nope, q_rope, kv_pool, int(N), kv_indptr, kv_indices,
+                                                          out_cache_loc, custom_mask, mask_indptr, int(B),
+                                                          int(q_len), int(H), float(scale), int(units), out, lse,
+                                                          stream))
 
 
 REPORT_MAX_OUT, REPORT_MAX_LSE, REPORT_ROWS, REPORT_BAD, REPORT_WORDS = 0, 1, 2, 3, 4

@@ -28,6 +28,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "mla_verify.h"
@@ -1410,6 +1412,7 @@ extern "C" const char* mla_verify_status_string(int status) {
     case MLA_VERIFY_ERR_NSPLIT: return "nsplit outside [1, 1024]";
     case MLA_VERIFY_ERR_WORKSPACE: return "workspace NULL, misaligned or too small";
     case MLA_VERIFY_ERR_LAUNCH: return "kernel launch failed";
+    case MLA_VERIFY_ERR_SCRATCH: return "sizes need more workspace than the no-alloc call's static scratch holds";
     default: return "unknown status";
   }
 }
@@ -1641,4 +1644,60 @@ extern "C" int mla_verify_attn_balanced(const void* q_nope, const void* q_rope, 
                                mask_indptr, B, q_len, H, scale, units, ws, stream);
   if (rc != MLA_VERIFY_OK) return rc;
   return launch_balanced_combine(ws, kv_pool, N, B, units, out, lse, stream);
+}
+
+// ---- the entry point that allocates nothing: mla_verify_attn_balanced on a static workspace
+
+// The workspace of mla_verify_attn_balanced_noalloc. Each device the code object is loaded on has
+// its own copy. In host code this name is a host-side stand-in, never a device address: the
+// kernels get the device address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[MLA_VERIFY_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 256;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// Device address of the current device's copy of `scratch`, resolved on the first call there.
+int scratch_address(void** addr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_VERIFY_ERR_LAUNCH;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MLA_VERIFY_ERR_LAUNCH;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *addr = p;
+  return MLA_VERIFY_OK;
+}
+
+}  // namespace
+
+extern "C" int mla_verify_attn_balanced_noalloc(const void* q_nope, const void* q_rope, const void* kv_pool,
+                                                int64_t N, const int32_t* kv_indptr, const int32_t* kv_indices,
+                                                const int32_t* out_cache_loc, const uint8_t* custom_mask,
+                                                const int32_t* mask_indptr, int B, int q_len, int H, float scale,
+                                                int units, void* out, float* lse, hipStream_t stream) {
+  if (inputs_null(q_nope, q_rope, kv_pool, kv_indptr, out_cache_loc, custom_mask, mask_indptr) || !out || !lse)
+    return MLA_VERIFY_ERR_NULL;
+  if (!sizes_ok(B, q_len, H) || N < 1 || N > INT32_MAX || !(scale > 0.0f) || !isfinite(scale))
+    return MLA_VERIFY_ERR_SHAPE;
+  if (B > MLA_VERIFY_BALANCED_MAX_B) return MLA_VERIFY_ERR_SHAPE;
+  if (units < B || units > MLA_VERIFY_MAX_UNITS) return MLA_VERIFY_ERR_NSPLIT;
+  if (!balanced_sizes_ok(B, q_len, H, units)) return MLA_VERIFY_ERR_SHAPE;
+  const size_t need = mla_verify_attn_balanced_workspace_size(B, q_len, H, units);
+  if (need > MLA_VERIFY_NOALLOC_SCRATCH_BYTES) return MLA_VERIFY_ERR_SCRATCH;
+  void* ws = nullptr;
+  int rc = scratch_address(&ws);
+  if (rc != MLA_VERIFY_OK) return rc;
+  const BalancedLaunch lw = balanced_workspace(ws, B, q_len, H, units);
+  rc = launch_balanced_partial(q_nope, q_rope, kv_pool, N, kv_indptr, kv_indices, out_cache_loc, custom_mask,
+                               mask_indptr, B, q_len, H, scale, units, lw, stream);
+  if (rc != MLA_VERIFY_OK) return rc;
+  return launch_balanced_combine(lw, kv_pool, N, B, units, out, lse, stream);
 }

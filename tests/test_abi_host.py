@@ -27,6 +27,7 @@ def test_library_exports_every_declared_function():
                           "mla_verify_tree_mask", "mla_verify_kv_compact",
                           "mla_verify_attn_balanced", "mla_verify_attn_balanced_partial",
                           "mla_verify_attn_balanced_combine", "mla_verify_attn_balanced_workspace_size",
+                          "mla_verify_attn_balanced_noalloc",
                           "mla_verify_attn_check", "mla_verify_attn_validate",
                           "mla_verify_attn_check_workspace_size", "mla_verify_attn_validate_workspace_size"}
     for n in names:
@@ -47,7 +48,7 @@ def test_workspace_size():
 
 
 def test_status_strings():
-    for code in range(-5, 1):
+    for code in range(-6, 1):
         assert pkg.status_string(code)
     assert pkg.status_string(7) == "unknown status"
 
@@ -173,3 +174,22 @@ def test_check_and_validate_validate_before_any_hip_call():
     assert pkg.validate_raw(**{**v, "sample_stride": 0}) == -2
     assert pkg.validate_raw(**{**v, "nsplit": 0}) == -3
     assert pkg.validate_raw(**{**v, "workspace_bytes": ws - 1}) == -4
+
+
+def test_noalloc_validation_before_any_hip_call():
+    """The no-alloc entry point rejects bad arguments, and sizes whose balanced workspace exceeds
+    its static scratch, before touching the device (so these calls run without a GPU)."""
+    base = dict(q_nope=FAKE, q_rope=FAKE, kv_pool=FAKE, N=100, kv_indptr=FAKE, kv_indices=FAKE, out_cache_loc=FAKE,
+                custom_mask=FAKE, mask_indptr=FAKE, B=4, q_len=16, H=64, scale=0.07, units=32, out=FAKE, lse=FAKE,
+                stream=None)
+    assert pkg.balanced_noalloc_raw(**{**base, "out": None}) == -1
+    assert pkg.balanced_noalloc_raw(**{**base, "lse": None}) == -1
+    assert pkg.balanced_noalloc_raw(**{**base, "q_len": 0}) == -2
+    assert pkg.balanced_noalloc_raw(**{**base, "scale": float("nan")}) == -2
+    assert pkg.balanced_noalloc_raw(**{**base, "units": 3}) == -3
+    assert pkg.balanced_noalloc_raw(**{**base, "units": 4097}) == -3
+    # the ragged four-request batch of 64 heads and 16 tokens fits at 32 units, not at 128
+    assert pkg.balanced_workspace_size(4, 16, 64, 32) <= pkg.NOALLOC_SCRATCH_BYTES
+    assert pkg.balanced_workspace_size(4, 16, 64, 128) > pkg.NOALLOC_SCRATCH_BYTES
+    assert pkg.balanced_noalloc_raw(**{**base, "units": 128}) == -6
+    assert "static scratch" in pkg.status_string(-6)
