@@ -67,9 +67,9 @@ typedef enum {
 /*
  * Bytes of workspace mla_verify_attn needs for these sizes ("From Capture Safety to MoE
  * Ceiling", "The Architecture of Capture Safety": the workspace is allocated once, outside
- * the step). It holds one partial per (request, split, draft token, head): the running max
- * and sum (2 floats), the unnormalised 512-wide accumulator (512 floats) and the top record
- * (8 bytes).
+ * the step). It holds one partial per (request, split, draft token, head): the running max,
+ * the sum and a power-of-two scale (a 16-byte record), the 512-wide accumulator (512 fp16
+ * values) and the top record (8 bytes).
  * Returns 0 when an argument is out of range (B, q_len, H < 1; nsplit outside [1, 1024]).
  */
 size_t mla_verify_attn_workspace_size(int B, int q_len, int H, int nsplit);
@@ -131,11 +131,13 @@ int mla_verify_attn(const void *q_nope, const void *q_rope, const void *kv_pool,
  * mla_verify_attn_combine runs the reduction kernel of the same section on those partials and
  * writes out and lse. Between the two calls the workspace holds, for every (b, s, i, h), the
  * split's running max m (base-2 units of the scaled score, -inf for an empty or fully masked
- * split), its sum l of 2^(score*log2(e) - m), its unnormalised 512-wide accumulator (every
- * probability rounded to bf16 before it multiplies a value row, as the matrix cores take it) and
- * its top record: the exact probability p of the split's largest visible score (same base as l)
- * and the pool slot (already clamped into [0, N)) of that column's 576-wide row. Laid out as
- * float2 ml[B][nsplit][q_len*H], then float acc[B][nsplit][q_len*H][512], then
+ * split), its sum l of 2^(score*log2(e) - m), its 512-wide accumulator A (every probability
+ * rounded to bf16 before it multiplies a value row, as the matrix cores take it, summed in fp32)
+ * stored as fp16 values of A * 2^-e, with e chosen per row so that the largest |A| * 2^-e lies in
+ * [2^14, 2^15) (one rounding to 11 significant bits, no overflow for any finite A), and its top
+ * record: the exact probability p of the split's largest visible score (same base as l) and the
+ * pool slot (already clamped into [0, N)) of that column's 576-wide row. Laid out as
+ * float4 ml[B][nsplit][q_len*H] = {m, l, 2^e, 0}, then fp16 acc[B][nsplit][q_len*H][512], then
  * int32x2 top[B][nsplit][q_len*H] = {bits of p, slot}, each region starting at a 256-byte
  * boundary. The combine adds w_s (p - bf16(p)) times the first 512 values of pool row `slot`
  * for every split whose p w_s is at least 1/32 of the row's final sum (exact probability restored
@@ -180,7 +182,7 @@ int mla_verify_attn_combine(const void *workspace, size_t workspace_bytes, const
  *
  * The workspace holds the plan (split_info int32x4 [units]: {request, first column, end column, 0}
  * of each split, {-1, 0, 0, 0} if unused; then split_start int32 [B + 1]: the running sum of n_b),
- * then float2 ml [units][q_len*H], float acc [units][q_len*H][512] and int32x2 top
+ * then float4 ml [units][q_len*H], fp16 acc [units][q_len*H][512] and int32x2 top
  * [units][q_len*H] partials as described for mla_verify_attn_partial (split split_start[b] + s of
  * request b at block split_start[b] + s), each region 256-byte aligned.
  * mla_verify_attn_balanced_partial writes the plan and the partials (for B <= 64 the partial

@@ -83,6 +83,8 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -578,8 +580,8 @@ struct PartialArgs {
   const int32_t* mask_indptr;
   int B, q_len, H;
   float scale_log2;
-  float2* ws_ml;
-  float* ws_acc;
+  float4* ws_ml;
+  uint16_t* ws_acc;
   int2* ws_top;
 };
 
@@ -592,7 +594,7 @@ struct PartialLds {
 };
 
 // Columns [c_begin, c_end) (c_begin < c_end) of request b for the 128 query rows of row tile rt:
-// writes the (m, l) and accumulator partials of those rows at partial row offset `part`.
+// writes the (m, l, 2^e) records and fp16 accumulator partials of those rows at partial row offset `part`.
 template <bool kWide>
 __device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds& lds, int b, int c_begin,
                                           int c_end, int rt, size_t part) {
@@ -602,8 +604,8 @@ __device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds
   const int32_t* __restrict__ kv_indices = a.kv_indices;
   const int32_t* __restrict__ out_cache_loc = a.out_cache_loc;
   const uint8_t* __restrict__ custom_mask = a.custom_mask;
-  float2* __restrict__ ws_ml = a.ws_ml;
-  float* __restrict__ ws_acc = a.ws_acc;
+  float4* __restrict__ ws_ml = a.ws_ml;
+  uint16_t* __restrict__ ws_acc = a.ws_acc;
   const int H = a.H, q_len = a.q_len;
   const int lane = threadIdx.x & 63;
   const int w = wave_uniform(threadIdx.x >> 6);
@@ -616,7 +618,7 @@ __device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds
   const int own_row0 = rt * kRowsPerWG + w * kBlockRows;
   const int own_row = own_row0 + (lane & 31);
   if (c_begin >= c_end) {
-    if (own_row < R && g == 0) ws_ml[part + own_row] = make_float2(-INFINITY, 0.0f);
+    if (own_row < R && g == 0) ws_ml[part + own_row] = make_float4(-INFINITY, 0.0f, 0.0f, 0.0f);
     return;
   }
 
@@ -777,20 +779,53 @@ __device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds
     }
   }
 
-  // ---- partial write: (m_ref, l) and the unnormalised 512-wide accumulator of the wave's rows
+  // ---- partial write: (m_ref, l, 2^e) and the row's 512-wide accumulator times 2^-e in fp16, with e
+  // taken from the row's largest |value| so that it lands in [2^14, 2^15): one rounding to 11
+  // significant bits and no overflow whatever the values' range (half the bytes of fp32 partials).
   const float l_row = pair_sum(st.l_lane);
-  if (own_row < R) {
-    float* dst = ws_acc + (part + own_row) * kLatent;
+  float amax = 0.0f;
+#pragma unroll
+  for (int eb = 0; eb < kEBlocks; ++eb) {
+#pragma unroll
+    for (int j = 0; j < 16; j += 2)
+      asm volatile("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(amax) : "v"(amax), "v"(oacc[eb][j]), "v"(oacc[eb][j + 1]));
+  }
+  amax = pair_max(amax);
+  // amax = f 2^fe with f in [0.5, 1): the scale 2^(15 - fe) puts it in [2^14, 2^15); capped so that
+  // the factor stays a normal float (rows below 2^-111 then keep smaller values, still exact in range)
+  const int fe = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) : 15;
+  const int sh = min(15 - fe, 126);
+  const float up = __builtin_amdgcn_ldexpf(1.0f, sh);
+  {
+    // rows past R (the last block's padding) convert and swap like the others, unstored: the lane
+    // swap runs with the whole wave active
+    uint16_t* dst = ws_acc + (part + min(own_row, R - 1)) * kLatent;
 #pragma unroll
     for (int eb = 0; eb < kEBlocks; ++eb) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const f32x4 val = {oacc[eb][4 * k], oacc[eb][4 * k + 1], oacc[eb][4 * k + 2], oacc[eb][4 * k + 3]};
-        *reinterpret_cast<f32x4*>(dst + 32 * eb + 8 * k + 4 * g) = val;
+      for (int m = 0; m < 2; ++m) {
+        // values 8m .. 8m+3 are columns 32 eb + 16 m + 4 g + (0..3), values 8m+4 .. 8m+7 columns
+        // 32 eb + 16 m + 8 + 4 g + (0..3); one swap with the partner lane (g = 1 - g) leaves lane g
+        // with columns 32 eb + 16 m + 8 g + (0..7), stored as one 16-byte write
+        uint32_t lo[2], hi[2];
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          const f16x2 a = __builtin_convertvector(
+              (f32x2){oacc[eb][8 * m + 2 * d] * up, oacc[eb][8 * m + 2 * d + 1] * up}, f16x2);
+          const f16x2 c = __builtin_convertvector(
+              (f32x2){oacc[eb][8 * m + 4 + 2 * d] * up, oacc[eb][8 * m + 4 + 2 * d + 1] * up}, f16x2);
+          const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, a),
+                                                          __builtin_bit_cast(uint32_t, c), false, false);
+          lo[d] = r[0];
+          hi[d] = r[1];
+        }
+        if (own_row < R)
+          *reinterpret_cast<u32x4*>(dst + 32 * eb + 16 * m + 8 * g) = (u32x4){lo[0], lo[1], hi[0], hi[1]};
       }
     }
   }
-  if (own_row < R && g == 0) ws_ml[part + own_row] = make_float2(st.m_ref, l_row);
+  if (own_row < R && g == 0)
+    ws_ml[part + own_row] = make_float4(st.m_ref, l_row, __builtin_amdgcn_ldexpf(1.0f, -sh), 0.0f);
 }
 
 #define PARTIAL_LDS_DECL                                                          \
@@ -811,8 +846,8 @@ verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restric
                       const int32_t* __restrict__ out_cache_loc,
                       const uint8_t* __restrict__ custom_mask,
                       const int32_t* __restrict__ mask_indptr, int B, int q_len, int H,
-                      float scale_log2, int nsplit, int n_rt, float2* __restrict__ ws_ml,
-                      float* __restrict__ ws_acc, int2* __restrict__ ws_top) {
+                      float scale_log2, int nsplit, int n_rt, float4* __restrict__ ws_ml,
+                      uint16_t* __restrict__ ws_acc, int2* __restrict__ ws_top) {
   PARTIAL_LDS_DECL
   const PartialArgs a = {q_nope, q_rope, kv_pool, N, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
                          B, q_len, H, scale_log2, ws_ml, ws_acc, ws_top};
@@ -1010,8 +1045,8 @@ verify_partial_balanced_kernel(const __bf16* __restrict__ q_nope, const __bf16* 
                                const uint8_t* __restrict__ custom_mask,
                                const int32_t* __restrict__ mask_indptr, int B, int q_len, int H,
                                float scale_log2, int units, int n_rt, int fused_plan, int4* __restrict__ split_info,
-                               int* __restrict__ split_start, float2* __restrict__ ws_ml,
-                               float* __restrict__ ws_acc, int2* __restrict__ ws_top) {
+                               int* __restrict__ split_start, float4* __restrict__ ws_ml,
+                               uint16_t* __restrict__ ws_acc, int2* __restrict__ ws_top) {
   PARTIAL_LDS_DECL
   const PartialArgs a = {q_nope, q_rope, kv_pool, N, kv_indptr, kv_indices, out_cache_loc, custom_mask, mask_indptr,
                          B, q_len, H, scale_log2, ws_ml, ws_acc, ws_top};
@@ -1039,17 +1074,35 @@ verify_partial_balanced_kernel(const __bf16* __restrict__ q_nope, const __bf16* 
   run_split<kWide>(a, lds, b, c_begin, c_end, rt, (size_t)j * (q_len * H));
 }
 
+// Adds one split's partial to a combine lane's 8 columns: weight 2^(m - M) on the sum l, and on the
+// 8 stored fp16 values (the accumulator times 2^-e) the weight times 2^e (st = {m, l, 2^e, 0}). An
+// empty or fully masked split (m = -inf) adds nothing and its data is not used.
+__device__ __forceinline__ void add_partial(const float4& st, const u32x4& x, float M, f32x4& acc0, f32x4& acc1,
+                                            float& den) {
+  const bool live = st.x != -INFINITY;
+  const float wgt = live ? __builtin_amdgcn_exp2f(st.x - M) : 0.0f;
+  den += live ? wgt * st.y : 0.0f;
+  const float wv = wgt * st.z;
+  const f16x8 h = __builtin_bit_cast(f16x8, x);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    acc0[k] += live ? wv * (float)h[k] : 0.0f;
+    acc1[k] += live ? wv * (float)h[4 + k] : 0.0f;
+  }
+}
+
 // kWaves waves per query row (b, r): weights w_s = 2^(m_s - M) over the non-empty partials,
-// out = sum w_s acc_s / sum w_s l_s, lse = (M + log2 sum w_s l_s) * ln 2. One wave per row (4 rows
+// out = sum w_s acc_s / sum w_s l_s, lse = (M + log2 sum w_s l_s) * ln 2, with acc_s read as its
+// stored fp16 values times 2^e_s. One wave per row (4 rows
 // per workgroup) suits many rows (the ragged 185k batch, 4096 rows); more waves per row keep the chip
 // busy when there are few rows and many splits (72 rows x 256 splits with one wave each left most
 // CUs idle and walked 256 splits serially: 95 us, against 11 us with sixteen waves; the quarter-row
 // kernel below takes that case now). The kernel is
 // bound by memory round trips, so it keeps them few:
-//  1. lane k of wave w reads the (m, l) pair and top record of split w*64 + k (and the maxima of
+//  1. lane k of wave w reads the (m, l, 2^e) record and top record of split w*64 + k (and the maxima of
 //     splits further on): the row max M;
 //  2. lane k owns output columns [8k, 8k+8); wave w takes splits w, w + kWaves, ..., 4 at a time,
-//     every (m, l) and accumulator load of a batch issued together (an empty
+//     every record and accumulator load of a batch issued together (an empty
 //     split's accumulator was never written: it is read, then discarded by a select);
 //  3. the sum is reduced over the row's waves; each wave adds back, for its own splits whose top
 //     column holds at least 1/32 of the row's sum, w_s (p - bf16(p)) times that column's value row
@@ -1063,7 +1116,7 @@ constexpr int combine_block_waves() { return kWaves == 1 ? 4 : kWaves; }
 
 template <bool kBalanced, int kWaves>
 __global__ void __launch_bounds__(combine_block_waves<kWaves>() * 64)
-verify_combine_kernel(const float2* __restrict__ ws_ml, const float* __restrict__ ws_acc,
+verify_combine_kernel(const float4* __restrict__ ws_ml, const uint16_t* __restrict__ ws_acc,
                       const int2* __restrict__ ws_top, const uint8_t* __restrict__ kv_pool, int N, int B, int R,
                       int nsplit_or_units, const int* __restrict__ split_start, __bf16* __restrict__ out,
                       float* __restrict__ lse) {
@@ -1085,11 +1138,11 @@ verify_combine_kernel(const float2* __restrict__ ws_ml, const float* __restrict_
     nsplit = nsplit_or_units;
     first = (size_t)b * nsplit;
   }
-  const float2* ml = ws_ml + first * R + r;
+  const float4* ml = ws_ml + first * R + r;
   const int2* top = ws_top + first * R + r;
-  // 1. split w*64 + lane: (m, l) and top record in registers; the max over every split
+  // 1. split w*64 + lane: (m, l, 2^e) and top records in registers; the max over every split
   const int s_own = w * 64 + lane;
-  const float2 st_own = s_own < nsplit ? ml[(size_t)s_own * R] : make_float2(-INFINITY, 0.0f);
+  const float4 st_own = s_own < nsplit ? ml[(size_t)s_own * R] : make_float4(-INFINITY, 0.0f, 0.0f, 0.0f);
   const int2 top_own = s_own < nsplit ? top[(size_t)s_own * R] : make_int2(0, 0);
   float M = st_own.x;
   for (int s = s_own + kWaves * 64; s < nsplit; s += kWaves * 64) M = fmaxf(M, ml[(size_t)s * R].x);
@@ -1113,29 +1166,21 @@ verify_combine_kernel(const float2* __restrict__ ws_ml, const float* __restrict_
   // 2. weighted accumulators and sum over this wave's splits
   f32x4 acc0 = {}, acc1 = {};
   float den = 0.0f;
-  const float* base = ws_acc + (first * R + r) * kLatent + lane * 8;
+  const uint16_t* base = ws_acc + (first * R + r) * kLatent + lane * 8;
   const size_t split_stride = (size_t)R * kLatent;
   constexpr int kU = 4;  // splits per batch (8 measured slower: the registers cut occupancy to 3 waves)
   for (int s0 = w; s0 < nsplit; s0 += kWaves * kU) {
-    float2 st[kU];
-    f32x4 x0[kU], x1[kU];
+    float4 st[kU];
+    u32x4 x[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int s = s0 + kWaves * u;
       const bool valid = s < nsplit;
-      st[u] = valid ? ml[(size_t)s * R] : make_float2(-INFINITY, 0.0f);
-      const f32x4* src = reinterpret_cast<const f32x4*>(base + (size_t)(valid ? s : 0) * split_stride);
-      x0[u] = src[0];
-      x1[u] = src[1];
+      st[u] = valid ? ml[(size_t)s * R] : make_float4(-INFINITY, 0.0f, 0.0f, 0.0f);
+      x[u] = *reinterpret_cast<const u32x4*>(base + (size_t)(valid ? s : 0) * split_stride);
     }
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const bool live = st[u].x != -INFINITY;  // empty or fully masked split: weight 0, data unused
-      const float wgt = live ? __builtin_amdgcn_exp2f(st[u].x - M) : 0.0f;
-      den += live ? wgt * st[u].y : 0.0f;
-      acc0 += live ? wgt * x0[u] : f32x4{};
-      acc1 += live ? wgt * x1[u] : f32x4{};
-    }
+    for (int u = 0; u < kU; ++u) add_partial(st[u], x[u], M, acc0, acc1, den);
   }
   // 3. the row's sum, then the exact top probabilities of this wave's splits
   float den_row = den;
@@ -1147,7 +1192,7 @@ verify_combine_kernel(const float2* __restrict__ ws_ml, const float* __restrict_
     for (int k = 1; k < kWaves; ++k) den_row += red_den[k];
   }
   for (int s = s_own; s - lane < nsplit; s += kWaves * 64) {  // wave-uniform bound
-    float2 st = st_own;
+    float4 st = st_own;
     int2 t = top_own;
     if (s != s_own && s < nsplit) {  // splits past the first 64 kWaves (rare): read their records
       st = ml[(size_t)s * R];
@@ -1204,7 +1249,7 @@ verify_combine_kernel(const float2* __restrict__ ws_ml, const float* __restrict_
 constexpr int kQuarterWaves = 8;
 template <bool kBalanced>
 __global__ void __launch_bounds__(kQuarterWaves * 64)
-verify_combine_quarter_kernel(const float2* __restrict__ ws_ml, const float* __restrict__ ws_acc,
+verify_combine_quarter_kernel(const float4* __restrict__ ws_ml, const uint16_t* __restrict__ ws_acc,
                               const int2* __restrict__ ws_top, const uint8_t* __restrict__ kv_pool, int N, int B,
                               int R, int nsplit_or_units,
                               const int* __restrict__ split_start, __bf16* __restrict__ out,
@@ -1228,11 +1273,11 @@ verify_combine_quarter_kernel(const float2* __restrict__ ws_ml, const float* __r
     nsplit = nsplit_or_units;
     first = (size_t)b * nsplit;
   }
-  const float2* ml = ws_ml + first * R + r;
+  const float4* ml = ws_ml + first * R + r;
   const int2* top = ws_top + first * R + r;
-  // 1. split w*64 + lane: (m, l) and top record in registers; the max over every split
+  // 1. split w*64 + lane: (m, l, 2^e) and top records in registers; the max over every split
   const int s_own = w * 64 + lane;
-  const float2 st_own = s_own < nsplit ? ml[(size_t)s_own * R] : make_float2(-INFINITY, 0.0f);
+  const float4 st_own = s_own < nsplit ? ml[(size_t)s_own * R] : make_float4(-INFINITY, 0.0f, 0.0f, 0.0f);
   const int2 top_own = s_own < nsplit ? top[(size_t)s_own * R] : make_int2(0, 0);
   float M = st_own.x;
   for (int s = s_own + kQuarterWaves * 64; s < nsplit; s += kQuarterWaves * 64) M = fmaxf(M, ml[(size_t)s * R].x);
@@ -1255,30 +1300,22 @@ verify_combine_quarter_kernel(const float2* __restrict__ ws_ml, const float* __r
   // 2. weighted accumulators and sum over this lane group's splits
   f32x4 acc0 = {}, acc1 = {};
   float den = 0.0f;
-  const float* base = ws_acc + (first * R + r) * kLatent + col0;
+  const uint16_t* base = ws_acc + (first * R + r) * kLatent + col0;
   const size_t split_stride = (size_t)R * kLatent;
   constexpr int kU = 4;
   constexpr int kStride = 4 * kQuarterWaves;  // splits between consecutive ones of a lane group
   for (int s0 = 4 * w + sq; s0 < nsplit; s0 += kStride * kU) {
-    float2 st[kU];
-    f32x4 x0[kU], x1[kU];
+    float4 st[kU];
+    u32x4 x[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int s = s0 + kStride * u;
       const bool valid = s < nsplit;
-      st[u] = valid ? ml[(size_t)s * R] : make_float2(-INFINITY, 0.0f);
-      const f32x4* src = reinterpret_cast<const f32x4*>(base + (size_t)(valid ? s : 0) * split_stride);
-      x0[u] = src[0];
-      x1[u] = src[1];
+      st[u] = valid ? ml[(size_t)s * R] : make_float4(-INFINITY, 0.0f, 0.0f, 0.0f);
+      x[u] = *reinterpret_cast<const u32x4*>(base + (size_t)(valid ? s : 0) * split_stride);
     }
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const bool live = st[u].x != -INFINITY;  // empty or fully masked split: weight 0, data unused
-      const float wgt = live ? __builtin_amdgcn_exp2f(st[u].x - M) : 0.0f;
-      den += live ? wgt * st[u].y : 0.0f;
-      acc0 += live ? wgt * x0[u] : f32x4{};
-      acc1 += live ? wgt * x1[u] : f32x4{};
-    }
+    for (int u = 0; u < kU; ++u) add_partial(st[u], x[u], M, acc0, acc1, den);
   }
   // the four lane groups of the wave: every lane ends with the wave's sums for its columns
 #pragma unroll
@@ -1298,7 +1335,7 @@ verify_combine_quarter_kernel(const float2* __restrict__ ws_ml, const float* __r
 #pragma unroll
   for (int k = 1; k < kQuarterWaves; ++k) den_row += red_den[k];
   for (int s = s_own; s - lane < nsplit; s += kQuarterWaves * 64) {  // wave-uniform bound
-    float2 st = st_own;
+    float4 st = st_own;
     int2 t = top_own;
     if (s != s_own && s < nsplit) {
       st = ml[(size_t)s * R];
@@ -1352,16 +1389,16 @@ constexpr long long kCombineFewRows = 512;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Per partial row: (m, l), the 512 accumulators, and the top record {exact top probability (float
-// bits), pool slot of its value row}; each region 256-byte aligned.
+// Per partial row: {m, l, 2^e, 0}, the 512 accumulators times 2^-e in fp16, and the top record
+// {exact top probability (float bits), pool slot of its value row}; each region 256-byte aligned.
 struct WorkspaceLayout {
   size_t ml_bytes, acc_bytes, top_bytes;
 };
 
 WorkspaceLayout workspace_layout(int B, int q_len, int H, int nsplit) {
   const size_t rows = (size_t)B * nsplit * q_len * H;
-  return {align_up(rows * sizeof(float2), MLA_VERIFY_WORKSPACE_ALIGN),
-          align_up(rows * kLatent * sizeof(float), MLA_VERIFY_WORKSPACE_ALIGN),
+  return {align_up(rows * sizeof(float4), MLA_VERIFY_WORKSPACE_ALIGN),
+          align_up(rows * kLatent * sizeof(uint16_t), MLA_VERIFY_WORKSPACE_ALIGN),
           align_up(rows * sizeof(int2), MLA_VERIFY_WORKSPACE_ALIGN)};
 }
 
@@ -1371,7 +1408,7 @@ bool sizes_ok(int B, int q_len, int H) {
   return rows <= (1LL << 24) && (long long)B * rows <= (1LL << 30);
 }
 
-// Balanced workspace: the plan (split_info int32x4 [units], split_start int32 [B + 1]), then (m, l),
+// Balanced workspace: the plan (split_info int32x4 [units], split_start int32 [B + 1]), then (m, l, 2^e),
 // accumulators and top records for `units` partial row blocks, each region 256-byte aligned.
 struct BalancedLayout {
   size_t plan_bytes, ml_bytes, acc_bytes, top_bytes;
@@ -1380,8 +1417,8 @@ struct BalancedLayout {
 BalancedLayout balanced_layout(int B, int q_len, int H, int units) {
   const size_t rows = (size_t)units * q_len * H;
   return {align_up((size_t)units * sizeof(int4) + (size_t)(B + 1) * sizeof(int), MLA_VERIFY_WORKSPACE_ALIGN),
-          align_up(rows * sizeof(float2), MLA_VERIFY_WORKSPACE_ALIGN),
-          align_up(rows * kLatent * sizeof(float), MLA_VERIFY_WORKSPACE_ALIGN),
+          align_up(rows * sizeof(float4), MLA_VERIFY_WORKSPACE_ALIGN),
+          align_up(rows * kLatent * sizeof(uint16_t), MLA_VERIFY_WORKSPACE_ALIGN),
           align_up(rows * sizeof(int2), MLA_VERIFY_WORKSPACE_ALIGN)};
 }
 
@@ -1420,8 +1457,8 @@ extern "C" const char* mla_verify_status_string(int status) {
 namespace {
 
 struct Launch {
-  float2* ws_ml;
-  float* ws_acc;
+  float4* ws_ml;
+  uint16_t* ws_acc;
   int2* ws_top;
   int R;
 };
@@ -1438,7 +1475,7 @@ int check_common(int B, int q_len, int H, int nsplit, const void* workspace, siz
 Launch split_workspace(void* workspace, int B, int q_len, int H, int nsplit) {
   const WorkspaceLayout lay = workspace_layout(B, q_len, H, nsplit);
   uint8_t* w = static_cast<uint8_t*>(workspace);
-  return {reinterpret_cast<float2*>(w), reinterpret_cast<float*>(w + lay.ml_bytes),
+  return {reinterpret_cast<float4*>(w), reinterpret_cast<uint16_t*>(w + lay.ml_bytes),
           reinterpret_cast<int2*>(w + lay.ml_bytes + lay.acc_bytes), q_len * H};
 }
 
@@ -1484,8 +1521,8 @@ int launch_combine(const Launch& ws, const void* kv_pool, int64_t N, int B, int 
 struct BalancedLaunch {
   int* split_start;
   int4* split_info;
-  float2* ws_ml;
-  float* ws_acc;
+  float4* ws_ml;
+  uint16_t* ws_acc;
   int2* ws_top;
   int R;
 };
@@ -1504,7 +1541,7 @@ BalancedLaunch balanced_workspace(void* workspace, int B, int q_len, int H, int 
   const BalancedLayout lay = balanced_layout(B, q_len, H, units);
   uint8_t* w = static_cast<uint8_t*>(workspace);
   return {reinterpret_cast<int*>(w + (size_t)units * sizeof(int4)), reinterpret_cast<int4*>(w),
-          reinterpret_cast<float2*>(w + lay.plan_bytes), reinterpret_cast<float*>(w + lay.plan_bytes + lay.ml_bytes),
+          reinterpret_cast<float4*>(w + lay.plan_bytes), reinterpret_cast<uint16_t*>(w + lay.plan_bytes + lay.ml_bytes),
           reinterpret_cast<int2*>(w + lay.plan_bytes + lay.ml_bytes + lay.acc_bytes), q_len * H};
 }
 

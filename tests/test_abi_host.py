@@ -35,9 +35,10 @@ def test_library_exports_every_declared_function():
 
 
 def test_workspace_size():
-    # (m, l) float2 + 512 fp32 + an 8-byte top record per (b, split, token, head), each region padded to 256 bytes
+    # {m, l, 2^e, 0} float4 + 512 fp16 + an 8-byte top record per (b, split, token, head), each region padded
+    # to 256 bytes
     rows = 2 * 16 * 9 * 8
-    expect = -(-rows * 8 // 256) * 256 + -(-rows * 2048 // 256) * 256 + -(-rows * 8 // 256) * 256
+    expect = -(-rows * 16 // 256) * 256 + -(-rows * 1024 // 256) * 256 + -(-rows * 8 // 256) * 256
     assert pkg.workspace_size(2, 9, 8, 16) == expect
     assert pkg.workspace_size(0, 9, 8, 16) == 0
     assert pkg.workspace_size(1, 0, 8, 16) == 0
@@ -123,7 +124,7 @@ def test_kv_compact_validates_before_any_hip_call():
 def test_balanced_workspace_size_and_validation():
     rows = 40 * 16 * 64
     plan = -(-(40 * 16 + 5 * 4) // 256) * 256
-    expect = plan + -(-rows * 8 // 256) * 256 + -(-rows * 2048 // 256) * 256 + -(-rows * 8 // 256) * 256
+    expect = plan + -(-rows * 16 // 256) * 256 + -(-rows * 1024 // 256) * 256 + -(-rows * 8 // 256) * 256
     assert pkg.balanced_workspace_size(4, 16, 64, 40) == expect
     assert pkg.balanced_workspace_size(4, 16, 64, 3) == 0          # fewer units than requests
     assert pkg.balanced_workspace_size(4, 16, 64, 4097) == 0
