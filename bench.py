@@ -6,13 +6,17 @@ one batch of seeded synthetic inputs already resident in HBM. The default worklo
 B=4 batch with prefixes 4096/32768/120000/185000, q_len 16, H 64, scattered slots in a 2M-row
 pool, under the balanced schedule with a budget of one workgroup per CU (units = CUs / 128-row
 tiles = 32 on MI355X); --schedule per-request --nsplit 64 runs nsplit splits per request instead.
-`value` is the effective KV bandwidth (sum of L_b * 1152 bytes per step / time per step);
-`ms_per_step` is the wall-clock time per step over the timed region.
+
+Timing: parity of the run's inputs is checked against the oracle first; then each of the `steps`
+timed steps reads a 1 GiB scrub buffer (evicting L2 and the MALL, outside the events) and replays
+the partial and the combine graphs between HIP events on one stream. `value` is the effective KV
+bandwidth (sum of L_b * 1152 bytes per step / median step time), `ms_per_step` the median step. The
+one-graph step is also replayed 50 times cold (scrub before each) and 50 times hot, reported as
+median/p10/p90.
 
 The roofline object covers the dominant kernel (the partial kernel): its algorithmic flops (or
-bytes, when the workload sits below the MFMA ridge) per launch over its average duration, timed
-with HIP events on the stream it runs on. cpu_baseline times the fp64 CPU oracle on a bounded
-sample of rows of the same workload and scales it to the whole step.
+bytes, when the workload sits below the MFMA ridge) per launch over its mean duration in the timed
+steps. cpu_baseline runs the fp64 CPU oracle over the whole step once on all host cores.
 """
 from __future__ import annotations
 
@@ -103,56 +107,61 @@ class Workload:
         self.partial(stream)
         self.combine(stream)
 
-    def time_steps(self, stream, steps, warmup, scrub=None):
-        """Eager steps with HIP events around each kernel; returns per-step wall and kernel times (us)."""
+    def capture(self, stream):
+        """Three graphs on `stream`: the whole step (partial + combine), the partial alone and the
+        combine alone (the last two let events bracket each kernel inside a timed step)."""
         torch = self.torch
-        for _ in range(warmup):
-            self.step(stream)
-        torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-        if scrub is None:
-            t0 = time.perf_counter()
-            for k in range(steps):
-                evs[k][0].record(stream)
-                self.partial(stream)
-                evs[k][1].record(stream)
-                self.combine(stream)
-                evs[k][2].record(stream)
-            torch.cuda.synchronize()
-            wall = (time.perf_counter() - t0) / steps * 1e6
-        else:
-            for k in range(steps):
-                # evict the KV rows from L2 and the MALL outside the events: a 1 GiB read on the bench
-                # stream itself (a fill on another stream would run alongside the step, and a fill on
-                # this one would leave dirty lines whose write-back lands inside the step)
-                with torch.cuda.stream(stream):
-                    scrub.view(torch.int64).sum()
-                evs[k][0].record(stream)
-                self.partial(stream)
-                evs[k][1].record(stream)
-                self.combine(stream)
-                evs[k][2].record(stream)
-            torch.cuda.synchronize()
-            wall = None
-        part = [evs[k][0].elapsed_time(evs[k][1]) * 1e3 for k in range(steps)]
-        comb = [evs[k][1].elapsed_time(evs[k][2]) * 1e3 for k in range(steps)]
-        stepu = [evs[k][0].elapsed_time(evs[k][2]) * 1e3 for k in range(steps)]
-        return wall, part, comb, stepu
-
-    def graph_us_per_step(self, stream, replays, warmup=3):
-        torch = self.torch
-        g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(stream):
+            self.step(stream)  # first launches outside capture (lazy module loading)
+        torch.cuda.synchronize()
+        self.g_step, self.g_part, self.g_comb = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        for g, fn in ((self.g_step, self.step), (self.g_part, self.partial), (self.g_comb, self.combine)):
             with torch.cuda.graph(g, stream=stream):
-                self.step(stream)
+                fn(stream)
+        torch.cuda.synchronize()
+
+    def _replay(self, g, stream):
+        with self.torch.cuda.stream(stream):
+            g.replay()
+
+    def kernel_split(self, stream, n, scrub):
+        """n eager steps, each a scrub then the partial and combine kernels with HIP events on `stream`
+        around each (an eager launch puts ~5 us less between its events than a graph launch does, so
+        these give the kernels' own durations); per-step times (us): step, partial, combine."""
+        torch = self.torch
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+        torch.cuda.synchronize()
+        for k in range(n):
+            scrub_l2(torch, scrub, stream)
+            evs[k][0].record(stream)
+            self.partial(stream)
+            evs[k][1].record(stream)
+            self.combine(stream)
+            evs[k][2].record(stream)
+        torch.cuda.synchronize()
+        stepu = [evs[k][0].elapsed_time(evs[k][2]) * 1e3 for k in range(n)]
+        part = [evs[k][0].elapsed_time(evs[k][1]) * 1e3 for k in range(n)]
+        comb = [evs[k][1].elapsed_time(evs[k][2]) * 1e3 for k in range(n)]
+        return stepu, part, comb
+
+    def graph_replays(self, stream, n, scrub=None, warmup=10):
+        """The step graph replayed n times between HIP events: cold (a scrub before each replay,
+        outside the events) or hot (back to back) when scrub is None; per-replay times (us)."""
+        torch = self.torch
         for _ in range(warmup):
-            g.replay()
+            if scrub is not None:
+                scrub_l2(torch, scrub, stream)
+            self._replay(self.g_step, stream)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(replays):
-            g.replay()
+        for k in range(n):
+            if scrub is not None:
+                scrub_l2(torch, scrub, stream)
+            evs[k][0].record(stream)
+            self._replay(self.g_step, stream)
+            evs[k][1].record(stream)
         torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / replays * 1e6
+        return [evs[k][0].elapsed_time(evs[k][1]) * 1e3 for k in range(n)]
 
     def parity(self, nrows, seed=0):
         """Sampled rows (corners + random) of the last step against the fp64 oracle."""
@@ -176,33 +185,108 @@ class Workload:
         return dict(rows=int(len(rows)), max_abs=err, rel_l2=rel, lse_abs=lerr, ok=bool(ok))
 
 
-def cpu_baseline(inp, alg, wl_name, seconds):
-    """The fp64 oracle on the host cores, on rows sampled from the workload, scaled to a full step."""
-    import numpy as np
+def scrub_l2(torch, scrub, stream):
+    """Evict L2 and the MALL with a 1 GiB read on the bench stream itself. A read, not a write: a fill
+    leaves dirty lines whose write-back would land inside the next timed step, and a fill on another
+    stream would overlap it."""
+    with torch.cuda.stream(stream):
+        scrub.view(torch.int64).sum()
 
+
+def settle(wk, stream, scrub, replays=30, seconds=0.04):
+    """Untimed step replays (each after a scrub) until at least `replays` of them and `seconds` have
+    passed. Power management holds the GPU clock low for the first few dozen launches of this
+    MFMA-heavy step after an idle period: rocprofv3 counters of the partial kernel show the same
+    GRBM_GUI_ACTIVE cycles per dispatch throughout, at ~1.85 GHz effective for the first launches
+    and ~2.05 GHz from about the 30th on. Other busy work beforehand does not help: memory-bound work
+    does not raise the clock, and a burst of bf16 GEMMs leaves it lower for a while."""
+    torch = wk.torch
+    torch.cuda.synchronize()
+    t0, n = time.perf_counter(), 0
+    while n < replays or time.perf_counter() - t0 < seconds:
+        scrub_l2(torch, scrub, stream)
+        wk._replay(wk.g_step, stream)
+        n += 1
+        if n % 10 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
+def hbm_probe(torch, dev, stream, gib=2.0, reps=10):
+    """Stream probe for context: a plain device copy (read + write) and a read-only reduction of
+    `gib` GiB, best of `reps`, in GB/s (bytes moved / event time)."""
+    n = int(gib * (1 << 30))
+    a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    res = {}
+    for name, fn, nbytes in (("copy_GBs", lambda: b.copy_(a), 2 * n),
+                             ("read_GBs", lambda: a.view(torch.int64).sum(), n)):
+        best = None
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3
+            best = us if best is None else min(best, us)
+        res[name] = nbytes / (best * 1e-6) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    res["bytes"] = n
+    res["note"] = "plain torch copy_ and int64 sum, best of %d; context for the 8 TB/s nominal peak" % reps
+    return res
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_seconds(inp, nthreads):
+    """Wall time of one full fp64 oracle run (every row of the step) on `nthreads` host threads."""
     import oracle
     import workloads as W
     pool, ki, oc = W.compact_inputs(inp)
     args = oracle.inputs_args(inp, pool, ki, oc)
+    t0 = time.perf_counter()
+    oracle.attn(*args, nthreads=nthreads)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(inp, alg, wl_name):
+    """The fp64 CPU oracle over the whole step (every (b, i, h) row), once, on all host cores."""
     cores = len(os.sched_getaffinity(0))
-    lengths = [p + inp.q_len for p in inp.prefixes]
-    rng = np.random.default_rng(1)
-    done_rows, done_cols, spent = 0, 0, 0.0
-    batch = max(cores, 1)
-    while spent < seconds:
-        rows = np.stack([rng.integers(0, inp.B, batch), rng.integers(0, inp.q_len, batch),
-                         rng.integers(0, inp.H, batch)], axis=1).astype(np.int32)
-        t0 = time.perf_counter()
-        oracle.attn_rows(*args, rows=rows, nthreads=cores)
-        spent += time.perf_counter() - t0
-        done_rows += len(rows)
-        done_cols += int(sum(lengths[b] for b in rows[:, 0]))
-    all_cols = inp.q_len * inp.H * sum(lengths)
-    t_step = spent * all_cols / done_cols
-    value = alg["kv_bytes"] / t_step / 1e9
-    return dict(value=value, unit="GB/s", cores=cores, kind="oracle",
-                sample=f"{done_rows} random (b,i,h) rows of {wl_name} ({done_cols} row-columns, {spent:.1f} s); "
-                       f"full step estimated at {t_step:.1f} s by column count", us_per_step=t_step * 1e6)
+    t = oracle_seconds(inp, cores)
+    return dict(value=alg["kv_bytes"] / t / 1e9, unit="GB/s", cores=cores, kind="oracle",
+                sample=f"the whole {wl_name} step (all {inp.B * inp.q_len * inp.H} query rows), one run of "
+                       f"{t:.1f} s on {cores} threads ({cpu_model()})", us_per_step=t * 1e6, seconds=t)
+
+
+def oracle_timings(names):
+    """Full oracle runs of the smaller configurations: median of 3 on all host cores, and one
+    1-thread run for the three smallest."""
+    import workloads as W
+    cores = len(os.sched_getaffinity(0))
+    out = {}
+    for k, name in enumerate(names):
+        wl = W.CONFIGS[name]
+        inp = W.make_inputs(wl, layout=wl.layout)
+        runs = sorted(oracle_seconds(inp, cores) for _ in range(3))
+        rec = {"seconds_all_cores": runs[1], "cores": cores,
+               "kv_GBs_all_cores": algorithmic(inp)["kv_bytes"] / runs[1] / 1e9}
+        if k < 3:
+            rec["seconds_1_thread"] = oracle_seconds(inp, 1)
+        out[name] = rec
+    out["cpu_model"] = cpu_model()
+    return out
 
 
 def stats(xs):
@@ -428,10 +512,8 @@ def step_floor_us(alg):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    # the partial kernel speeds up over its first ~40 launches in a fresh process (a kernel trace of
-    # the 185k batch: 1000-1100 us at first, a steady ~820 us after), so the default warmup covers that
-    ap.add_argument("--warmup", type=int, default=60)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="ragged4_185k_h64")
     ap.add_argument("--layout", default=None)
     ap.add_argument("--nsplit", type=int, default=None,
@@ -441,7 +523,6 @@ def main():
                          "per-request: nsplit splits per request (mla_verify_attn)")
     ap.add_argument("--units", type=int, default=None,
                     help="balanced schedule: split budget (default: CUs / 128-row tiles, one workgroup per CU)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true", help="skip the 16k/65k configuration sweep")
     ap.add_argument("--parity-rows", type=int, default=48)
@@ -477,33 +558,67 @@ def main():
     print(f"[bench] {wl.name} layout={layout} schedule={args.schedule} "
           f"{'units' if balanced else 'nsplit'}={nsplit}", file=sys.stderr, flush=True)
     wk = Workload(wl, layout, nsplit, dev, balanced=balanced)
-    wall, part, comb, stepu = wk.time_steps(stream, args.steps, args.warmup)
-    print(f"[bench] timed {args.steps} steps: {wall:.1f} us/step", file=sys.stderr, flush=True)
+    scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    # parity of this run's inputs before any timing
+    with torch.cuda.stream(stream):
+        wk.step(stream)
     parity = wk.parity(args.parity_rows)
+    print(f"[bench] parity on {parity['rows']} sampled rows: ok={parity['ok']}", file=sys.stderr, flush=True)
+    wk.capture(stream)
+    settled = settle(wk, stream, scrub)
+    for _ in range(args.warmup):
+        scrub_l2(torch, scrub, stream)
+        wk._replay(wk.g_step, stream)
+    # the timed region: exactly `steps` steps, each a scrub (outside the events) then one replay of the
+    # step graph between HIP events
+    t0 = time.perf_counter()
+    timed = wk.graph_replays(stream, args.steps, scrub=scrub, warmup=0)
+    wall = time.perf_counter() - t0
+    step_s = stats(timed)
+    print(f"[bench] timed {args.steps} steps: median {step_s['median']:.1f} us/step", file=sys.stderr, flush=True)
+    # the kernels' own durations (eager launches, same scrub), and the protocol's 50-replay distributions
+    e_step, part, comb = wk.kernel_split(stream, max(args.steps, 20), scrub)
+    part_s, comb_s, eager_s = stats(part), stats(comb), stats(e_step)
+    cold = stats(wk.graph_replays(stream, 50, scrub=scrub, warmup=0))
+    hot = stats(wk.graph_replays(stream, 50))
     check = None if args.no_next else measure_check(wk, stream)
-    # as long a warmup as the eager steps: the first few dozen launches of the partial kernel run slower
-    graph_us = wk.graph_us_per_step(stream, max(args.steps, 20), warmup=args.warmup)
-    part_s, comb_s = stats(part), stats(comb)
     alg = wk.alg
-    value = alg["kv_bytes"] / (wall * 1e-6) / 1e9
+    med = step_s["median"]
+    value = alg["kv_bytes"] / (med * 1e-6) / 1e9
     floor = step_floor_us(alg)
     roof = roofline_for(wk, part_s["mean"])
     traffic, traffic_src = measured_traffic(wl.name, ("u" if balanced else "ns") + str(nsplit))
     roof["traffic"] = traffic
     roof["traffic_source"] = traffic_src
+    roof["duration_us"] = part_s["mean"]
+    roof["duration_source"] = ("mean of HIP events around eager launches of the partial kernel, each after "
+                               "a 1 GiB scrub")
     result = {
         "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": wall / 1e3, "us_per_step": wall, "higher_is_better": True,
+        "warmup": args.warmup, "ms_per_step": med / 1e3, "us_per_step": med, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "prefixes": list(wl.prefixes), "q_len": wl.q_len, "H": wl.H,
                    "pool_rows": wl.N, "layout": layout, "schedule": args.schedule,
                    ("units" if balanced else "nsplit"): nsplit, "seed": wl.seed,
                    "scale": "1/sqrt(192)", "parallelism": "single GPU"},
+        "timing": ("each timed step: a 1 GiB scrub read (outside the events), then one replay of the captured "
+                   "step graph (partial + combine) between HIP events on one stream; value and ms_per_step use "
+                   "the median step. kernels_us: eager launches with events around each kernel, same scrub"),
+        "timed_region_wall_s": wall,
+        "settle_replays": settled,
+        "settle": ("untimed step replays before the warmup steps (at least 30 and 40 ms): the GPU clock ramps "
+                   "from ~1.85 to ~2.05 GHz over the first few dozen launches of the step"),
         "roofline": roof,
-        "kernels_us": {"partial": part_s, "combine": comb_s, "step_events": stats(stepu)},
-        "graph_us_per_step": graph_us,
-        "step_floor_us": floor, "step_roofline_frac": floor / wall,
-        "tflops_step": alg["flops"] / (wall * 1e-6) / 1e12,
+        "step_us": step_s,
+        "kernels_us": {"partial": part_s, "combine": comb_s, "eager_step": eager_s},
+        "graph_step_cold_us": cold, "graph_step_hot_us": hot,
+        "graph_protocol": "one-graph step: 10 warm-up replays, then 50 replays between HIP events, each after a "
+                          "1 GiB scrub (cold); hot = 50 back-to-back replays",
+        "step_floor_us": floor, "step_roofline_frac": floor / med,
+        "algorithmic_GBs": alg["step_bytes"] / (med * 1e-6) / 1e9,
+        "algorithmic_frac_hbm": alg["step_bytes"] / (med * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "tflops_step": alg["flops"] / (med * 1e-6) / 1e12,
+        "tflops_frac_mfma": alg["flops"] / (med * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFS,
         "parity_sampled": parity,
     }
     if check is not None:
@@ -511,6 +626,7 @@ def main():
     main_inp = wk.inp
     del wk
     torch.cuda.empty_cache()
+    result["hbm_probe"] = hbm_probe(torch, dev, stream)
 
     if not args.no_next:
         print("[bench] tree mask builder", file=sys.stderr, flush=True)
@@ -521,55 +637,56 @@ def main():
         torch.cuda.empty_cache()
 
     if not args.no_others:
-        others = []
-        # the ragged batch under both schedules (hot, back-to-back steps)
-        for sched, ns in (("per-request", 32), ("per-request", 64), ("per-request", 128),
-                          ("balanced", 32), ("balanced", 64), ("balanced", 128)):
-            print(f"[bench] sweep {wl.name} {sched} {ns}", file=sys.stderr, flush=True)
-            ow = Workload(wl, layout, ns, dev, balanced=sched == "balanced")
-            hot_wall, hp, hc, hs = ow.time_steps(stream, 20, 3)
-            others.append({"workload": wl.name, "layout": layout, "schedule": sched,
-                           ("units" if sched == "balanced" else "nsplit"): ns, "hot_us_per_step": hot_wall,
-                           "partial_us_hot": stats(hp)["mean"], "combine_us_hot": stats(hc)["mean"],
-                           "partial_roofline": roofline_for(ow, stats(hp)["mean"])})
-            del ow
-            torch.cuda.empty_cache()
-        scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         def auto_units(w):  # one workgroup per CU: the balanced schedule's default budget
             return max(w.B, cus // -(-w.q_len * w.H // 128))
 
-        sweep = [("16k_h64", "contiguous", "per-request", 16), ("16k_h64", "scattered", "per-request", 16),
-                 ("16k_h64", "scattered", "per-request", 32), ("16k_h64", "scattered", "per-request", 64),
-                 ("65k_h8", "scattered", "per-request", 16), ("65k_h8", "scattered", "per-request", 64),
-                 ("4k_h64", "scattered", "per-request", 16)]
-        sweep += [(n, lay, "balanced", auto_units(W.CONFIGS[n])) for n, lay in
-                  (("16k_h64", "contiguous"), ("16k_h64", "scattered"), ("65k_h8", "scattered"),
-                   ("4k_h64", "scattered"))]
+        sweep = [(n, lay, "balanced", auto_units(W.CONFIGS[n])) for n, lay in
+                 (("16k_h64", "scattered"), ("16k_h64", "contiguous"), ("65k_h8", "scattered"),
+                  ("4k_h64", "scattered"), ("tiny_256_h8", "scattered"))]
+        sweep += [(wl.name, layout, "per-request", 64), (wl.name, layout, "balanced", 64),
+                  ("16k_h64", "scattered", "per-request", 16), ("16k_h64", "scattered", "per-request", 32),
+                  ("16k_h64", "scattered", "per-request", 64), ("16k_h64", "contiguous", "per-request", 16),
+                  ("65k_h8", "scattered", "per-request", 16), ("65k_h8", "scattered", "per-request", 64),
+                  ("4k_h64", "scattered", "per-request", 16), ("tiny_256_h8", "scattered", "per-request", 4)]
+        others = []
         for name, lay, sched, ns in sweep:
-            print(f"[bench] sweep {name} {lay} {sched} {ns}", file=sys.stderr, flush=True)
+            print(f"[bench] config {name} {lay} {sched} {ns}", file=sys.stderr, flush=True)
             ow = Workload(W.CONFIGS[name], lay, ns, dev, balanced=sched == "balanced")
-            hot_wall, hp, hc, hs = ow.time_steps(stream, 30, 5)
-            _, cp, cc, cs = ow.time_steps(stream, 20, 2, scrub=scrub)
+            ow.capture(stream)
+            settle(ow, stream, scrub, replays=10, seconds=0.02)
+            cold_o = stats(ow.graph_replays(stream, 50, scrub=scrub))
+            hot_o = stats(ow.graph_replays(stream, 50))
+            _, pcl, ccl = ow.kernel_split(stream, 25, scrub)
+            pc, cc = stats(pcl), stats(ccl)
             a = ow.alg
             fl = step_floor_us(a)
+            t = cold_o["median"]
+            tr, tr_src = measured_traffic(name, ("u" if sched == "balanced" else "ns") + str(ns))
+            pr = roofline_for(ow, pc["mean"])
+            pr["traffic"], pr["traffic_source"] = tr, tr_src
             others.append({
                 "workload": name, "layout": lay, "schedule": sched, ("units" if sched == "balanced" else "nsplit"): ns,
-                "hot_us_per_step": hot_wall, "hot_kv_GBs": a["kv_bytes"] / (hot_wall * 1e-6) / 1e9,
-                "cold_step_us_median": stats(cs)["median"],
-                "cold_kv_GBs": a["kv_bytes"] / (stats(cs)["median"] * 1e-6) / 1e9,
-                "partial_us_hot": stats(hp)["mean"], "partial_us_cold": stats(cp)["median"],
-                "combine_us_hot": stats(hc)["mean"],
-                "step_floor_us": fl, "roofline_frac_hot": fl / hot_wall, "roofline_frac_cold": fl / stats(cs)["median"],
-                "partial_roofline": roofline_for(ow, stats(hp)["mean"]),
+                "step_us_cold": cold_o, "step_us_hot": hot_o, "partial_us_cold": pc, "combine_us_cold": cc,
+                "kv_GBs_cold": a["kv_bytes"] / (t * 1e-6) / 1e9,
+                "algorithmic_GBs_cold": a["step_bytes"] / (t * 1e-6) / 1e9,
+                "algorithmic_frac_hbm": a["step_bytes"] / (t * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                "tflops_cold": a["flops"] / (t * 1e-6) / 1e12,
+                "tflops_frac_mfma": a["flops"] / (t * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFS,
+                "step_floor_us": fl, "roofline_frac_cold": fl / t, "roofline_frac_hot": fl / hot_o["median"],
+                "partial_roofline": pr,
             })
             del ow
             torch.cuda.empty_cache()
         result["other_configs"] = others
-        del scrub
+    del scrub
+    torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
-        print("[bench] cpu baseline", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(main_inp, alg, wl.name, args.cpu_seconds)
+        print("[bench] cpu baseline: the full oracle step", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(main_inp, alg, wl.name)
+        if not args.no_others:
+            print("[bench] oracle timings of the smaller configurations", file=sys.stderr, flush=True)
+            result["oracle_timings"] = oracle_timings(["tiny_256_h8", "4k_h64", "16k_h64", "65k_h8"])
     print(json.dumps(result), flush=True)
 
 
