@@ -622,21 +622,6 @@ __device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds
     return;
   }
 
-  // ---- the wave's query rows as MFMA B operands: k-step ks holds Q[row][16 ks + 8 g .. +8] (rows
-  // past R load row R-1 and are zeroed)
-  bf16x8 q[kRegSteps];
-  uint8_t* const q_lds = lds.q_rope + w * kQRopeBytes;
-  {
-    const int q_row = min(own_row, R - 1);
-    const bf16x8* qn = reinterpret_cast<const bf16x8*>(q_nope + ((size_t)b * R + q_row) * kLatent);
-    const bf16x8* qr = reinterpret_cast<const bf16x8*>(q_rope + ((size_t)b * R + q_row) * kRope);
-#pragma unroll
-    for (int ks = 0; ks < kRegSteps; ++ks) q[ks] = own_row < R ? qn[2 * ks + g] : bf16x8{};
-#pragma unroll
-    for (int j = 0; j < kSteps - kRegSteps; ++j)  // rope k-steps to LDS (read after the prologue barrier)
-      *reinterpret_cast<bf16x8*>(q_lds + 1024 * j + 16 * lane) = own_row < R ? qr[2 * j + g] : bf16x8{};
-  }
-
   Ctx x;
   x.mask_base = (size_t)a.mask_indptr[b];
   x.N = a.N;
@@ -661,9 +646,32 @@ __device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds
   x.n_meta = 1 + min((x.tok_last - x.tok_first + 1) / 2, kMetaExtra);
   x.scale_log2 = a.scale_log2;
   uint8_t* const meta = lds.meta + w * kMetaStages * kMetaBytes;
+  uint8_t* const q_lds = lds.q_rope + w * kQRopeBytes;
   uint8_t* const lds_kv = lds.kv;
   const Bufs bf = {lds_kv, meta, q_lds};
   const Glob gl = {kv_pool, kv_indices, out_cache_loc, custom_mask};
+
+  // ---- the metadata of the first four tiles, then the wave's query rows: the latent k-steps as MFMA
+  // B operands in registers (k-step ks holds Q[row][16 ks + 8 g .. +8]), the rope k-steps straight
+  // to LDS. Rows past R repeat row R-1 (their results are never written; a copy of a real row
+  // cannot set the rerun flag unless that row does). All of it is in flight at once and one wait
+  // in the prologue covers it; issued before the query registers are live, the metadata loads have
+  // their addresses at hand, not in spill slots whose reloads would each wait for every load.
+  issue_meta(x, kv_indices, out_cache_loc, custom_mask, c_begin, meta);
+  issue_meta(x, kv_indices, out_cache_loc, custom_mask, c_begin + kTile, meta + kMetaBytes);
+  issue_meta(x, kv_indices, out_cache_loc, custom_mask, c_begin + 2 * kTile, meta + 2 * kMetaBytes);
+  issue_meta(x, kv_indices, out_cache_loc, custom_mask, c_begin + 3 * kTile, meta + 3 * kMetaBytes);
+  bf16x8 q[kRegSteps];
+  {
+    const int q_row = min(own_row, R - 1);
+    const bf16x8* qn = reinterpret_cast<const bf16x8*>(q_nope + ((size_t)b * R + q_row) * kLatent);
+    const bf16x8* qr = reinterpret_cast<const bf16x8*>(q_rope + ((size_t)b * R + q_row) * kRope);
+#pragma unroll
+    for (int j = 0; j < kSteps - kRegSteps; ++j) dma_group<0>(qr + 2 * j + g, lds_addr(q_lds + 1024 * j));
+#pragma unroll
+    for (int ks = 0; ks < kRegSteps; ++ks) q[ks] = qn[2 * ks + g];
+  }
+
 
   // per-lane LDS offsets inside a tile, the same for every tile. K: logical chunk 2 b4 + g of tile row
   // lane & 31 (k-step ks uses b4 = ks % 4 plus 1024 (ks / 4)). V (transposed reads): the 16-lane
@@ -697,24 +705,25 @@ __device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds
     st.best_col = 0;
     st.over = false;
 
-    // ---- prologue: metadata of tiles 0-3, rows of tiles 0 and 1, then the scores of tile 0
-    issue_meta(x, kv_indices, out_cache_loc, custom_mask, c_begin, meta);
-    issue_meta(x, kv_indices, out_cache_loc, custom_mask, c_begin + kTile, meta + kMetaBytes);
+    // ---- prologue: the metadata of tiles 0-3 (issued above for the first pass), the rows of tiles 0
+    // and 1 (both tiles' addresses formed before either tile's loads go out, so no spill reload and
+    // its wait falls between them), then the scores of tile 0
+    if (pass > 0) {
+      issue_meta(x, kv_indices, out_cache_loc, custom_mask, c_begin, meta);
+      issue_meta(x, kv_indices, out_cache_loc, custom_mask, c_begin + kTile, meta + kMetaBytes);
+      issue_meta(x, kv_indices, out_cache_loc, custom_mask, c_begin + 2 * kTile, meta + 2 * kMetaBytes);
+      issue_meta(x, kv_indices, out_cache_loc, custom_mask, c_begin + 3 * kTile, meta + 3 * kMetaBytes);
+    }
     __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0): query rows and metadata
 #pragma unroll
     for (int ks = 0; ks < kRegSteps; ++ks) asm volatile("" ::"v"(q[ks]));  // query rows ready here
-    issue_kv<kWide>(x, kv_pool, meta, lds_kv);
-    issue_meta(x, kv_indices, out_cache_loc, custom_mask, c_begin + 2 * kTile, meta + 2 * kMetaBytes);
-    issue_kv<kWide>(x, kv_pool, meta + kMetaBytes, lds_kv + kTileBytes);
-    issue_meta(x, kv_indices, out_cache_loc, custom_mask, c_begin + 3 * kTile, meta + 3 * kMetaBytes);
-    // tiles 0 and 1 have landed (the metadata of tile 3 may still be in flight)
-    static_assert(kMetaExtra + 1 < 16, "vmcnt immediate");
-    if (x.n_meta == 1)
-      __builtin_amdgcn_s_waitcnt(1 | (0x7 << 4) | (0xF << 8));
-    else if (x.n_meta == 2)
-      __builtin_amdgcn_s_waitcnt(2 | (0x7 << 4) | (0xF << 8));
-    else
-      __builtin_amdgcn_s_waitcnt(3 | (0x7 << 4) | (0xF << 8));
+    {
+      const KvGather g0 = kv_gather_setup(x, kv_pool, meta, lds_kv);
+      const KvGather g1 = kv_gather_setup(x, kv_pool, meta + kMetaBytes, lds_kv + kTileBytes);
+      kv_gather_groups<kWide, 0, 9>(g0);
+      kv_gather_groups<kWide, 0, 9>(g1);
+    }
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0): tiles 0 and 1
     lds_barrier();
     f32x16 s_a, s_b;
     {
