@@ -593,11 +593,67 @@ struct PartialLds {
   int* over;
 };
 
+// A wave whose 32 rows all lie past R (the fourth wave at R = 72, the last two of a 64-row remainder)
+// has nothing to score, but the tile ring is filled by all four waves and every step ends in a
+// workgroup barrier. Such a wave keeps its share of the pipeline, step for step as tile_iter and
+// run_split do it: the same metadata and row loads, the same waits and the same barriers (one after
+// the prologue, one per tile, two for the rerun decision), and skips the products and the softmax.
+// It reports no overflow and follows the others into a second pass if one of them asks for it.
+template <bool kWide>
+__device__ __forceinline__ void run_loads_only(const Ctx& x, int c_begin, int ntiles, const Glob& gl, const Bufs& bf,
+                                            int* lds_over, int w) {
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      issue_meta(x, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, c_begin + k * kTile, bf.meta + k * kMetaBytes);
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0)
+    issue_kv<kWide>(x, gl.kv_pool, bf.meta, bf.kv);
+    issue_kv<kWide>(x, gl.kv_pool, bf.meta + kMetaBytes, bf.kv + kTileBytes);
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0)
+    lds_barrier();
+    for (int t = 0; t < ntiles; ++t) {
+      issue_kv<kWide>(x, gl.kv_pool, bf.meta + ((t + 2) % kMetaStages) * kMetaBytes,
+                      bf.kv + ((t + 2) % kBufs) * kTileBytes);
+      issue_meta(x, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, c_begin + (t + 4) * kTile,
+                 bf.meta + ((t + 4) % kMetaStages) * kMetaBytes);
+      // the row loads have landed; the x.n_meta metadata loads behind them may still be in flight
+      if (x.n_meta == 1)
+        __builtin_amdgcn_s_waitcnt(1 | (0x7 << 4) | (0xF << 8));
+      else if (x.n_meta == 2)
+        __builtin_amdgcn_s_waitcnt(2 | (0x7 << 4) | (0xF << 8));
+      else
+        __builtin_amdgcn_s_waitcnt(3 | (0x7 << 4) | (0xF << 8));
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0)
+    if ((threadIdx.x & 63) == 0) lds_over[w] = 0;
+    lds_barrier();
+    int any_over = 0;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) any_over |= lds_over[k];
+    lds_barrier();
+    if (!any_over) break;
+  }
+}
+
+// Where request b's inputs start: kv_indptr[b], its prefix length and mask_indptr[b].
+struct Request {
+  int kv_start, P;
+  int mask_base;
+};
+__device__ __forceinline__ Request load_request(const PartialArgs& a, int b) {
+  Request r;
+  r.kv_start = a.kv_indptr[b];
+  r.P = max(a.kv_indptr[b + 1] - r.kv_start, 0);
+  r.mask_base = a.mask_indptr[b];
+  return r;
+}
+
 // Columns [c_begin, c_end) (c_begin < c_end) of request b for the 128 query rows of row tile rt:
 // writes the (m, l, 2^e) records and fp16 accumulator partials of those rows at partial row offset `part`.
 template <bool kWide>
-__device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds& lds, int b, int c_begin,
-                                          int c_end, int rt, size_t part) {
+__device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds& lds, int b, const Request& rq,
+                                          int c_begin, int c_end, int rt, size_t part) {
   const __bf16* __restrict__ q_nope = a.q_nope;
   const __bf16* __restrict__ q_rope = a.q_rope;
   const uint8_t* __restrict__ kv_pool = a.kv_pool;
@@ -610,8 +666,8 @@ __device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds
   const int lane = threadIdx.x & 63;
   const int w = wave_uniform(threadIdx.x >> 6);
   const int R = q_len * H;
-  const int kv_start = a.kv_indptr[b];
-  const int P = max(a.kv_indptr[b + 1] - kv_start, 0);
+  const int kv_start = rq.kv_start;
+  const int P = rq.P;
   const int L = P + q_len;
 
   const int g = lane >> 5;  // k-group of the MFMA operands
@@ -623,7 +679,7 @@ __device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds
   }
 
   Ctx x;
-  x.mask_base = (size_t)a.mask_indptr[b];
+  x.mask_base = (size_t)rq.mask_base;
   x.N = a.N;
   x.b = b;
   x.q_len = q_len;
@@ -650,6 +706,10 @@ __device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds
   uint8_t* const lds_kv = lds.kv;
   const Bufs bf = {lds_kv, meta, q_lds};
   const Glob gl = {kv_pool, kv_indices, out_cache_loc, custom_mask};
+  if (own_row0 >= R) {  // wave-uniform: only padding rows
+    run_loads_only<kWide>(x, c_begin, (c_end - c_begin + kTile - 1) / kTile, gl, bf, lds.over, w);
+    return;
+  }
 
   // ---- the metadata of the first four tiles, then the wave's query rows: the latent k-steps as MFMA
   // B operands in registers (k-step ks holds Q[row][16 ks + 8 g .. +8]), the rope k-steps straight
@@ -865,13 +925,14 @@ verify_partial_kernel(const __bf16* __restrict__ q_nope, const __bf16* __restric
   const int b = sp.b, s = sp.s;
   const int R = a.q_len * a.H;
   // split bounds from the actual lengths (empty splits leave at once)
-  const int L = max(a.kv_indptr[b + 1] - a.kv_indptr[b], 0) + a.q_len;
+  const Request rq = load_request(a, b);
+  const int L = rq.P + a.q_len;
   int chunk = (L + nsplit - 1) / nsplit;
   chunk = (chunk + kTile - 1) / kTile * kTile;
   const int c_begin = s * chunk;
   const int c_end = min(L, c_begin + chunk);
   const size_t part = ((size_t)b * nsplit + s) * R;
-  run_split<kWide>(a, lds, b, c_begin, c_end, sp.rt, part);
+  run_split<kWide>(a, lds, b, rq, c_begin, c_end, sp.rt, part);
 }
 
 // ---- Balanced partition of the batch. Request b has T_b = ceil(L_b / 32) column tiles. With a
@@ -993,13 +1054,17 @@ __device__ __forceinline__ int wave_incl_scan_i32(int x, int lane) {
 // total / C > units; at the second it is at most total / C + B <= units), capped by the largest T_b.
 // Counts are 32-bit while every T_b < 2^25 (64 requests then total under 2^31 tiles); longer
 // requests (prefixes beyond 2^30 columns) take a 64-bit search over [1, max T_b]. Lanes b < B return
-// their request's running split count in *start_incl.
+// their request's running split count in *start_incl. The lane of request b also loads mask_indptr[b]
+// with its lengths, so the split's request bounds (*rq) cost no further round trip to memory.
 constexpr int kFusedPlanMaxB = 64;
-__device__ __forceinline__ int4 plan_split_wave(const int32_t* __restrict__ kv_indptr, int B, int q_len, int units,
-                                                int j, int lane, int* start_incl) {
-  int T = 0, Lb = 0;
+__device__ __forceinline__ int4 plan_split_wave(const int32_t* __restrict__ kv_indptr,
+                                                const int32_t* __restrict__ mask_indptr, int B, int q_len, int units,
+                                                int j, int lane, int* start_incl, Request* rq) {
+  int T = 0, Lb = 0, k0 = 0, m0 = 0;
   if (lane < B) {
-    const long long L = max((long long)kv_indptr[lane + 1] - (long long)kv_indptr[lane], 0LL) + q_len;
+    k0 = kv_indptr[lane];
+    m0 = mask_indptr[lane];
+    const long long L = max((long long)kv_indptr[lane + 1] - (long long)k0, 0LL) + q_len;
     T = (int)((L + kTile - 1) / kTile);
     Lb = (int)L;
   }
@@ -1035,6 +1100,9 @@ __device__ __forceinline__ int4 plan_split_wave(const int32_t* __restrict__ kv_i
   const int s_l = j - __builtin_amdgcn_readlane(excl, l), n_l = __builtin_amdgcn_readlane(n, l);
   const long long T_l = __builtin_amdgcn_readlane(T, l);
   const int L_l = __builtin_amdgcn_readlane(Lb, l);
+  rq->kv_start = __builtin_amdgcn_readlane(k0, l);
+  rq->P = L_l - q_len;
+  rq->mask_base = __builtin_amdgcn_readlane(m0, l);
   const int c0 = (int)((long long)s_l * T_l / n_l) * kTile;
   const int c1 = min(L_l, (int)((long long)(s_l + 1) * T_l / n_l) * kTile);
   return make_int4(l, c0, c1, 0);
@@ -1063,10 +1131,11 @@ verify_partial_balanced_kernel(const __bf16* __restrict__ q_nope, const __bf16* 
   const int j = xcd + 8 * (k / n_rt), rt = k % n_rt;
   if (j >= units) return;
   int4 info;  // {request, first column, end column}
+  Request rq;
   if (fused_plan) {
     const int lane = threadIdx.x & 63;
     int incl;
-    info = plan_split_wave(kv_indptr, B, q_len, units, j, lane, &incl);
+    info = plan_split_wave(kv_indptr, mask_indptr, B, q_len, units, j, lane, &incl, &rq);
     if (threadIdx.x < 64) {
       if (rt == 0 && lane == 0) split_info[j] = info;
       if (blockIdx.x == 0) {
@@ -1075,12 +1144,15 @@ verify_partial_balanced_kernel(const __bf16* __restrict__ q_nope, const __bf16* 
       }
     }
     info = make_int4(wave_uniform(info.x), wave_uniform(info.y), wave_uniform(info.z), 0);
+    if (info.x < 0) return;
+    rq = {wave_uniform(rq.kv_start), wave_uniform(rq.P), wave_uniform(rq.mask_base)};
   } else {
     info = split_info[j];
+    if (info.x < 0) return;
+    rq = load_request(a, info.x);
   }
-  if (info.x < 0) return;
   const int b = info.x, c_begin = info.y, c_end = info.z;
-  run_split<kWide>(a, lds, b, c_begin, c_end, rt, (size_t)j * (q_len * H));
+  run_split<kWide>(a, lds, b, rq, c_begin, c_end, rt, (size_t)j * (q_len * H));
 }
 
 // Adds one split's partial to a combine lane's 8 columns: weight 2^(m - M) on the sum l, and on the
