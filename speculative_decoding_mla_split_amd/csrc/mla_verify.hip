@@ -389,10 +389,11 @@ __device__ __forceinline__ uint32_t mask_word_uniform(const Ctx& x, int byte_val
 //   1. the score product of tile t+1 (36 products into s_nxt, K from ring slot (t+1) % 3), and
 //      between its products the softmax of tile t on s_cur: mask, maximum, reference, the
 //      numerators 2^(score - m_ref) rounded to bf16 for the PV product, and their exact sum; the
-//      row loads of tile t+2 go out between the first nine products;
+//      row loads of tile t+2 go out between the first nine products, the metadata loads of tile
+//      t+4 under the last ones (products 27-35 carry no softmax piece; between the PV products
+//      their address arithmetic cost ~0.7% more at the ragged 185k batch);
 //   2. the PV product of tile t (32 products, V^T from ring slot t % 3, two transposed reads per
-//      V operand, each feeding one product), with the metadata loads of tile t+4 among them (their
-//      address arithmetic costs less here than among the softmax pieces);
+//      V operand, each feeding one product);
 //   3. the wave waits for its row loads of tile t+2, then the workgroup barrier: after it, tile
 //      t+2 is in LDS for every wave, and every wave is done with ring slot t % 3, which the next
 //      step's row loads (tile t+3) refill.
@@ -519,6 +520,10 @@ __device__ __forceinline__ void tile_iter(const Ctx& x_in, int t, int c_begin, c
     // step to land (a CU's gathers of one tile complete about 3000 cycles after the first is issued,
     // wherever in the step they go; nine back to back before the first product cost more issue time)
     if constexpr (ks >= 0 && ks <= 8) kv_gather_group<kWide, ks>(gat);
+    // the metadata loads of tile t+4 under the last score products, which carry no softmax piece
+    if constexpr (ks == 27) issue_meta_part<0>(x, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, meta_c0, meta_dst);
+    if constexpr (ks == 30) issue_meta_part<1>(x, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, meta_c0, meta_dst);
+    if constexpr (ks == 33) issue_meta_part<2>(x, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, meta_c0, meta_dst);
 
     __builtin_amdgcn_sched_barrier(0);
   });
@@ -534,9 +539,6 @@ __device__ __forceinline__ void tile_iter(const Ctx& x_in, int t, int c_begin, c
       vf[(f + kVAhead) % (kVAhead + 1)] = load_v(kb_cur, v_off, (f + kVAhead) >> 4, (f + kVAhead) & 15);
     __builtin_amdgcn_sched_barrier(0);
     oacc[f & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[f % (kVAhead + 1)], pb[f >> 4], oacc[f & 15], 0, 0, 0);
-    if constexpr (f == 4) issue_meta_part<0>(x, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, meta_c0, meta_dst);
-    if constexpr (f == 8) issue_meta_part<1>(x, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, meta_c0, meta_dst);
-    if constexpr (f == 12) issue_meta_part<2>(x, gl.kv_indices, gl.out_cache_loc, gl.custom_mask, meta_c0, meta_dst);
     __builtin_amdgcn_sched_barrier(0);
   });
 
