@@ -100,11 +100,17 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // XOR swizzle inside a group: logical chunk k of tile row c sits in slot (k % 8) ^ swz(c) of group
-// k / 8. With all three row bits in the XOR, the eight rows of a region put any one logical chunk in
-// eight different 16-byte slots, and with the regions' 128-byte shift the 32-row K-operand reads
-// (one chunk of every row) hit every bank once; an XOR of bits 1-2 only left two rows per slot and
-// doubled the LDS cycles spent in bank conflicts (hardware counters: 4.65e7 vs 2.19e7 per launch).
-__host__ __device__ constexpr int swz(int c) { return c & 7; }
+// k / 8, with swz a permutation of the three low bits of the row (bit 1 of c drives bit 2 of the
+// slot). Bank of a 16-byte slot (64 banks of 4 bytes): 8 ((c / 8 + c) & 1) + ((k % 8) ^ swz(c)) in
+// units of 4 banks, the first term from the 128-byte row stride and the regions' 128-byte shift.
+//  - K operand reads (16 B per lane, 16 lanes a cycle: one chunk of 16 consecutive rows) hit 16
+//    different slots for any swz that is a bijection of c % 8.
+//  - V^T operand reads (ds_read_b64_tr_b16, 32 lanes a cycle: chunks 4 eb .. 4 eb + 3 of rows
+//    c0 .. c0 + 3, c0 % 4 == 0) need rows c0 and c0 + 2 (same half of the banks) in disjoint slot
+//    sets, i.e. swz(c0) ^ swz(c0 + 2) with bit 2 set. Plain c & 7 put both rows on the same four
+//    slots: a 2-way conflict on every V read, 4.38e7 conflict cycles per launch at the ragged 185k
+//    batch, two per read.
+__host__ __device__ constexpr int swz(int c) { return (c & 1) | ((c >> 1 & 1) << 2) | ((c >> 2 & 1) << 1); }
 
 __device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
