@@ -119,6 +119,54 @@ __host__ __device__ constexpr int tile_offset(int c, int k) {
   return (c / 8) * kRegionBytes + (k / 8) * kGroupBytes + (c % 8) * 128 + (((k % 8) ^ swz(c)) * 16);
 }
 
+// Per-lane parts of the MFMA operand addresses inside a tile, and the parts common to a wave.
+// K operand of k-step ks: logical chunk 2 (ks % 4) + g of tile row lane % 32, at k_lane_offset(lane,
+// ks % 4) + k_step_offset(ks). V^T operand of output block eb and k-step kk (two transposed 8-byte
+// reads, m = 0, 1): the 16-lane group G reads tile rows 16 kk + 8m + 4 (G / 2) + (k16 / 4), latent
+// columns 32 eb + 16 (G % 2) + 4 (k16 % 4) .. +3, i.e. logical chunk 4 eb + 2 (G % 2) + (k16 % 4) / 2,
+// at v_lane_offset(lane, eb % 2) + v_step_offset(kk, eb, m).
+__host__ __device__ constexpr int k_lane_offset(int lane, int b4) { return tile_offset(lane & 31, 2 * b4 + (lane >> 5)); }
+__host__ __device__ constexpr int k_step_offset(int ks) { return kGroupBytes * (ks / 4); }
+__host__ __device__ constexpr int v_lane_offset(int lane, int half) {
+  const int k16 = lane & 15, G = lane >> 4;
+  return tile_offset(4 * (G >> 1) + (k16 >> 2), 4 * half + 2 * (G & 1) + ((k16 & 3) >> 1)) + (k16 & 1) * 8;
+}
+__host__ __device__ constexpr int v_step_offset(int kk, int eb, int m) {
+  return 2 * kk * kRegionBytes + kGroupBytes * (eb >> 1) + m * kRegionBytes;
+}
+
+// Build-time proof that the operand reads meet no LDS bank conflict, on the bank model of gfx950
+// (64 banks of 4 bytes; a 16-byte-per-lane read is served 16 lanes a cycle, a transposed 8-byte read
+// 32 lanes a cycle): within each group of lanes served together, no two lanes touch the same bank.
+constexpr bool k_reads_conflict_free() {
+  for (int ks = 0; ks < kSteps; ++ks)
+    for (int l0 = 0; l0 < 64; l0 += 16) {
+      bool used[16] = {};
+      for (int lane = l0; lane < l0 + 16; ++lane) {
+        const int bank16 = ((k_lane_offset(lane, ks % 4) + k_step_offset(ks)) / 16) % 16;
+        if (used[bank16]) return false;
+        used[bank16] = true;
+      }
+    }
+  return true;
+}
+constexpr bool v_reads_conflict_free() {
+  for (int kk = 0; kk < 2; ++kk)
+    for (int eb = 0; eb < kLatent / 32; ++eb)
+      for (int m = 0; m < 2; ++m)
+        for (int l0 = 0; l0 < 64; l0 += 32) {
+          bool used[32] = {};
+          for (int lane = l0; lane < l0 + 32; ++lane) {
+            const int bank8 = ((v_lane_offset(lane, eb & 1) + v_step_offset(kk, eb, m)) / 8) % 32;
+            if (used[bank8]) return false;
+            used[bank8] = true;
+          }
+        }
+  return true;
+}
+static_assert(k_reads_conflict_free(), "K operand reads of the tile layout meet a bank conflict");
+static_assert(v_reads_conflict_free(), "transposed V operand reads of the tile layout meet a bank conflict");
+
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS reads and writes, then
 // s_barrier. Unlike __syncthreads() it does not drain the vector-memory counter, so direct-to-LDS
 // loads of later tiles stay in flight across it (their completion is awaited explicitly with
@@ -366,16 +414,16 @@ __device__ __forceinline__ bf16x8 q_operand(const bf16x8 (&q)[kRegSteps], const 
 // K operand of k-step ks (logical chunk 2ks + g of tile row lane & 31) at kb + k_off[ks % 4] +
 // 1024 (ks / 4); the four per-lane offsets do not change from tile to tile.
 __device__ __forceinline__ bf16x8 load_k(const uint8_t* kb, const int (&k_off)[4], int ks) {
-  return *reinterpret_cast<const bf16x8*>(kb + k_off[ks % 4] + kGroupBytes * (ks / 4));
+  return *reinterpret_cast<const bf16x8*>(kb + k_off[ks % 4] + k_step_offset(ks));
 }
 
 // V^T operand of output block eb (latent columns [32 eb, 32 eb + 32)) and k-step kk (tile columns
 // [16 kk, 16 kk + 16), permuted as the probabilities are): two transposed 8-byte reads, rows
 // 16 kk + 8m + v_row of latent chunk 4 eb + v_chunk (see run_split for v_off).
 __device__ __forceinline__ bf16x8 load_v(const uint8_t* kb, const int (&v_off)[2], int kk, int eb) {
-  const uint8_t* p0 = kb + v_off[eb & 1] + 2 * kk * kRegionBytes + kGroupBytes * (eb >> 1);
+  const uint8_t* p0 = kb + v_off[eb & 1] + v_step_offset(kk, eb, 0);
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + kRegionBytes));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kb + v_off[eb & 1] + v_step_offset(kk, eb, 1)));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -741,21 +789,12 @@ __device__ __forceinline__ void run_split(const PartialArgs& a, const PartialLds
   }
 
 
-  // per-lane LDS offsets inside a tile, the same for every tile. K: logical chunk 2 b4 + g of tile row
-  // lane & 31 (k-step ks uses b4 = ks % 4 plus 1024 (ks / 4)). V (transposed reads): the 16-lane
-  // group G reads tile rows 16kk + 8m + 4(G/2) + (k16/4), m = 0, 1, latent columns 32eb + 16(G%2) +
-  // 4(k16%4) .. +3, i.e. logical chunk 4eb + vc with vc = 2(G%2) + (k16%4)/2; v_off[eb % 2] plus
-  // 1024 (eb / 2) and the region offsets of rows 16kk + 8m.
+  // per-lane LDS offsets inside a tile, the same for every tile (k_lane_offset, v_lane_offset)
   int k_off[4], v_off[2];
 #pragma unroll
-  for (int b4 = 0; b4 < 4; ++b4) k_off[b4] = tile_offset(lane & 31, 2 * b4 + g);
-  {
-    const int k16 = lane & 15, G = lane >> 4;
-    const int v_row = 4 * (G >> 1) + (k16 >> 2);
-    const int v_chunk = 2 * (G & 1) + ((k16 & 3) >> 1);
-    v_off[0] = tile_offset(v_row, v_chunk) + (k16 & 1) * 8;
-    v_off[1] = tile_offset(v_row, 4 + v_chunk) + (k16 & 1) * 8;
-  }
+  for (int b4 = 0; b4 < 4; ++b4) k_off[b4] = k_lane_offset(lane, b4);
+  v_off[0] = v_lane_offset(lane, 0);
+  v_off[1] = v_lane_offset(lane, 1);
 
   const int ntiles = (c_end - c_begin + kTile - 1) / kTile;
   f32x16 oacc[kEBlocks];
